@@ -1,0 +1,225 @@
+"""MI355X (gfx950) token-level softmax cross-entropy: forward, backward and the
+fused forward + in-place backward, as hand-written HIP kernels behind a C ABI
+(include/ce_mi355x.h).
+
+This module only marshals torch tensors (device memory and the current HIP
+stream) into the C calls of the same names; every step of the computation runs
+in the library's kernels.  The operation is the "Fast Cross Entropy" loss of
+the pages (PyPI page "fms-acceleration-foak 0.7.4", kernel list) used as a
+drop-in replacement of a causal LM's cross-entropy (fms-acceleration PR #79,
+"Bug Fix to Model Patcher"): mean over valid tokens (fms-hf-tuning PR #280,
+"Early Version Of This Plugin"), ignore_index -100.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (CE_STATUS_LABEL_RANGE, CE_STATUS_SYNC_TIMEOUT, CeError)  # noqa: F401
+
+__all__ = [
+    "ce_workspace_bytes", "ce_workspace_init", "Workspace", "ce_forward", "ce_backward",
+    "ce_fwd_bwd_inplace", "cross_entropy", "FastCrossEntropyLoss", "CeError",
+]
+
+_DTYPES = {torch.float32: _lib.CE_DTYPE_F32, torch.bfloat16: _lib.CE_DTYPE_BF16,
+           torch.float16: _lib.CE_DTYPE_F16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"logits dtype {t.dtype} is not float32, bfloat16 or float16") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _rows(logits: torch.Tensor):
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [rows, vocab]")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous (stride(1) == 1)")
+    if not logits.is_cuda:
+        raise ValueError("logits must be on a GPU")
+    N, V = logits.shape
+    ld = logits.stride(0) if N > 1 else V
+    return N, V, ld
+
+
+def _labels(labels: torch.Tensor, N: int, device) -> torch.Tensor:
+    if labels.dtype != torch.int64 or labels.dim() != 1 or labels.numel() != N:
+        raise ValueError("labels must be a 1-D int64 tensor with one entry per row")
+    if labels.device != device or not labels.is_contiguous():
+        raise ValueError("labels must be contiguous on the logits' device")
+    return labels
+
+
+def ce_workspace_bytes(n_rows: int, vocab: int, chunk: int, dtype: torch.dtype) -> int:
+    n = _lib.load().ce_workspace_bytes(n_rows, vocab, chunk, _DTYPES[dtype])
+    if n == 0:
+        raise ValueError("no workspace size for these arguments")
+    return int(n)
+
+
+def ce_workspace_init(ws: torch.Tensor) -> None:
+    _lib.check(_lib.load().ce_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)), "ce_workspace_init")
+
+
+class Workspace:
+    """A device workspace that grows on demand; calls that share one must be
+    ordered on one stream."""
+
+    def __init__(self, device=None, nbytes: int = 0):
+        self.device = torch.device(device or "cuda")
+        self.buf = None
+        if nbytes:
+            self.reserve(nbytes)
+
+    def reserve(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            nbytes = max(nbytes, 4096)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            ce_workspace_init(self.buf)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _workspace(device, nbytes: int, ws: Workspace | None) -> torch.Tensor:
+    if ws is None:
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        ws = _default_ws.get(key)
+        if ws is None:
+            ws = _default_ws[key] = Workspace(device)
+    return ws.reserve(nbytes)
+
+
+def _outputs(N: int, device):
+    f32 = dict(dtype=torch.float32, device=device)
+    f64 = dict(dtype=torch.float64, device=device)
+    return {
+        "loss_mean": torch.empty(1, **f32),
+        "loss_rows": torch.empty(max(N, 1), **f32)[:N],
+        "lse_rows": torch.empty(max(N, 1), **f64)[:N],
+        "pcomp_rows": torch.empty(max(N, 1), **f64)[:N],
+        "n_valid": torch.empty(1, dtype=torch.int32, device=device),
+        "status": torch.empty(1, dtype=torch.int32, device=device),
+    }
+
+
+def check_status(out: dict) -> None:
+    """Synchronises and raises when the kernels flagged bad labels or a timeout."""
+    st = int(out["status"].item())
+    if st & CE_STATUS_SYNC_TIMEOUT:
+        raise RuntimeError("cross-entropy kernel: inter-workgroup wait timed out")
+    if st & CE_STATUS_LABEL_RANGE:
+        raise ValueError("a label is outside [0, vocab) and not ignore_index")
+
+
+def ce_forward(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100, chunk: int = 0,
+               workspace: Workspace | None = None, out: dict | None = None) -> dict:
+    """Loss mean, per-row loss / lse / (1 - p_label), n_valid and status."""
+    N, V, ld = _rows(logits)
+    dt = _dtype_code(logits)
+    labels = _labels(labels, N, logits.device)
+    out = out or _outputs(N, logits.device)
+    ws = _workspace(logits.device, ce_workspace_bytes(N, V, chunk, logits.dtype), workspace)
+    rc = _lib.load().ce_forward(
+        _ptr(logits), ld, _ptr(labels), N, V, dt, ignore_index, chunk, _ptr(out["loss_mean"]),
+        _ptr(out["loss_rows"]), _ptr(out["lse_rows"]), _ptr(out["pcomp_rows"]), _ptr(out["n_valid"]),
+        _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(logits.device))
+    _lib.check(rc, "ce_forward")
+    return out
+
+
+def ce_backward(logits: torch.Tensor, labels: torch.Tensor, lse_rows: torch.Tensor, pcomp_rows: torch.Tensor,
+                n_valid: torch.Tensor, dloss: torch.Tensor | None = None, ignore_index: int = -100,
+                grad: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient of dloss * L with respect to the logits (out of place unless
+    grad is the logits tensor itself)."""
+    N, V, ld = _rows(logits)
+    dt = _dtype_code(logits)
+    labels = _labels(labels, N, logits.device)
+    if grad is None:
+        grad = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    if grad.shape != logits.shape or grad.dtype != logits.dtype or grad.stride(1) != 1:
+        raise ValueError("grad must match the logits' shape and dtype with contiguous rows")
+    for t, d in ((lse_rows, torch.float64), (pcomp_rows, torch.float64), (n_valid, torch.int32)):
+        if t.dtype != d or not t.is_contiguous() or t.device != logits.device:
+            raise ValueError("saved statistics must be contiguous fp64 rows and an int32 count")
+    if dloss is not None and (dloss.dtype != torch.float32 or dloss.numel() != 1):
+        raise ValueError("dloss must be a one-element float32 tensor")
+    gld = grad.stride(0) if N > 1 else V
+    rc = _lib.load().ce_backward(
+        _ptr(logits), ld, _ptr(labels), _ptr(lse_rows), _ptr(pcomp_rows), _ptr(n_valid), _ptr(dloss), N, V, dt,
+        ignore_index, _ptr(grad), gld, _stream(logits.device))
+    _lib.check(rc, "ce_backward")
+    return grad
+
+
+def ce_fwd_bwd_inplace(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100, chunk: int = 0,
+                       dloss: torch.Tensor | None = None, workspace: Workspace | None = None,
+                       out: dict | None = None) -> dict:
+    """Forward outputs, with the gradient of dloss * L written over `logits`."""
+    N, V, ld = _rows(logits)
+    dt = _dtype_code(logits)
+    labels = _labels(labels, N, logits.device)
+    if dloss is not None and (dloss.dtype != torch.float32 or dloss.numel() != 1):
+        raise ValueError("dloss must be a one-element float32 tensor")
+    out = out or _outputs(N, logits.device)
+    ws = _workspace(logits.device, ce_workspace_bytes(N, V, chunk, logits.dtype), workspace)
+    rc = _lib.load().ce_fwd_bwd_inplace(
+        _ptr(logits), ld, _ptr(labels), N, V, dt, ignore_index, chunk, _ptr(dloss), _ptr(out["loss_mean"]),
+        _ptr(out["loss_rows"]), _ptr(out["lse_rows"]), _ptr(out["pcomp_rows"]), _ptr(out["n_valid"]),
+        _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(logits.device))
+    _lib.check(rc, "ce_fwd_bwd_inplace")
+    return out
+
+
+class _CrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, labels, ignore_index, chunk):
+        out = ce_forward(logits, labels, ignore_index, chunk)
+        ctx.save_for_backward(logits, labels, out["lse_rows"], out["pcomp_rows"], out["n_valid"])
+        ctx.ignore_index = ignore_index
+        return out["loss_mean"][0].to(logits.dtype)
+
+    @staticmethod
+    def backward(ctx, g):
+        logits, labels, lse, pcomp, n = ctx.saved_tensors
+        dloss = g.reshape(1).to(torch.float32)
+        grad = ce_backward(logits, labels, lse, pcomp, n, dloss, ctx.ignore_index)
+        return grad, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+                  chunk: int = 0) -> torch.Tensor:
+    """Token-mean softmax cross-entropy with autograd (logits [rows, vocab])."""
+    return _CrossEntropy.apply(logits, labels, ignore_index, chunk)
+
+
+class FastCrossEntropyLoss(torch.nn.Module):
+    """Drop-in for torch.nn.CrossEntropyLoss(ignore_index, reduction='mean')
+    over [..., vocab] logits and [...] int64 labels."""
+
+    def __init__(self, ignore_index: int = -100, reduction: str = "mean", chunk: int = 0,
+                 weight=None, label_smoothing: float = 0.0):
+        super().__init__()
+        if reduction != "mean" or weight is not None or label_smoothing != 0.0:
+            raise NotImplementedError("only reduction='mean' without weights or label smoothing")
+        self.ignore_index = ignore_index
+        self.chunk = chunk
+
+    def forward(self, logits: torch.Tensor, labels: torch.Tensor) -> torch.Tensor:
+        V = logits.shape[-1]
+        return cross_entropy(logits.reshape(-1, V), labels.reshape(-1), self.ignore_index, self.chunk)

@@ -1,0 +1,334 @@
+// ce_api.hip -- the C ABI declared in include/ce_mi355x.h: host-side argument
+// checks, workspace layout, kernel choice and launches on the caller's stream.
+// Every step of the computation runs in the kernels of ce_kernels.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "ce_kernels.h"
+#include "ce_mi355x.h"
+
+namespace {
+
+using cek::Args;
+typedef void (*KernelFn)(Args);
+
+#ifndef CE_POL
+#define CE_POL 1  // nontemporal loads, write-back stores
+#endif
+constexpr int kPol = CE_POL;
+constexpr int64_t kMaxRows = 0x7fffffff;
+
+int esize(int dtype) { return dtype == CE_DTYPE_F32 ? 4 : 2; }
+int epv(int dtype) { return 16 / esize(dtype); }
+
+// Largest row (or slab) the on-chip kernels hold: 1024 lanes x 16 vectors.
+int64_t max_slab(int dtype) { return (int64_t)1024 * 16 * epv(dtype); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Vocabulary split: C slabs of width `width` (C == 1: whole rows on chip).
+struct Split {
+  int64_t width;
+  int C;
+};
+bool make_split(int64_t V, int64_t chunk, int dtype, Split* s) {
+  const int64_t cap = max_slab(dtype);
+  int64_t w;
+  if (chunk == 0 || chunk >= V) w = (V <= cap) ? V : (dtype == CE_DTYPE_F32 ? 32768 : 65536);
+  else w = chunk;
+  if (w > cap) return false;
+  s->width = w;
+  s->C = (int)((V + w - 1) / w);
+  return true;
+}
+
+// Workspace: header, tagged per-row loss slots, then (chunked only) slab
+// partials, label logits and fp64 scratch for the row statistics.
+struct WsLayout {
+  size_t slots, slab_ms, slab_xy, lse_scratch, pcomp_scratch, total;
+};
+WsLayout ws_layout(int64_t N, const Split& sp) {
+  WsLayout L;
+  size_t off = cek::kWsHeaderBytes;
+  L.slab_ms = L.slab_xy = L.lse_scratch = L.pcomp_scratch = 0;
+  L.slots = off;
+  off += align256((size_t)N * sizeof(uint64_t));
+  if (sp.C > 1) {
+    L.slab_ms = off;
+    off += align256((size_t)N * sp.C * sizeof(double2));
+    L.slab_xy = off;
+    off += align256((size_t)N * sizeof(float));
+    L.lse_scratch = off;
+    off += align256((size_t)N * sizeof(double));
+    L.pcomp_scratch = off;
+    off += align256((size_t)N * sizeof(double));
+  }
+  L.total = off;
+  return L;
+}
+
+bool valid_dtype(int d) { return d == CE_DTYPE_F32 || d == CE_DTYPE_BF16 || d == CE_DTYPE_F16; }
+
+// Checks shared by every entry point.
+int check_shape(const void* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V, int dtype) {
+  if (!valid_dtype(dtype)) return CE_ERR_DTYPE;
+  if (N < 0 || N > kMaxRows || V < 1 || V > kMaxRows || ld < V) return CE_ERR_INVALID_ARG;
+  if (ld > ((int64_t)1 << 40)) return CE_ERR_INVALID_ARG;
+  if (N > 0 && (logits == nullptr || labels == nullptr)) return CE_ERR_INVALID_ARG;
+  if (((uintptr_t)logits) % esize(dtype) != 0) return CE_ERR_INVALID_ARG;
+  if (((uintptr_t)labels) % 8 != 0) return CE_ERR_INVALID_ARG;
+  return CE_OK;
+}
+
+int counters_for(int64_t N, int64_t G) {
+  int64_t k = (N + 1023) / 1024;
+  if (k < 1) k = 1;
+  if (k > cek::kMaxCounters) k = cek::kMaxCounters;
+  if (k > G) k = G;
+  return (int)k;
+}
+
+int launch(KernelFn fn, int64_t grid, int block, Args a, hipStream_t st) {
+  if (grid <= 0) return CE_OK;
+  if (grid > 0x7fffffff) return CE_ERR_UNSUPPORTED;
+  void* params[] = {&a};
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(block), params, 0, st);
+  return e == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+// ---- kernel tables ---------------------------------------------------------
+struct Cfg {
+  int nt, vpl;
+};
+// whole-row / slab capacities (16-byte vectors), smallest first
+const Cfg kCfgs[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 12}, {256, 16},
+                     {512, 12}, {512, 16}, {1024, 12}, {1024, 16}};
+
+Cfg pick_cfg(int64_t nvec_max) {
+  for (const Cfg& c : kCfgs)
+    if ((int64_t)c.nt * c.vpl >= nvec_max) return c;
+  return kCfgs[sizeof(kCfgs) / sizeof(kCfgs[0]) - 1];
+}
+
+#define CE_CFG_CASES(MAKE)                                                                          \
+  MAKE(256, 1) MAKE(256, 2) MAKE(256, 4) MAKE(256, 8) MAKE(256, 12) MAKE(256, 16) MAKE(512, 12) \
+  MAKE(512, 16) MAKE(1024, 12) MAKE(1024, 16)
+
+template <typename T, bool FUSED>
+KernelFn row16_fn(Cfg c) {
+#define MAKE(NT, VPL) \
+  if (c.nt == NT && c.vpl == VPL) return cek::row_kernel_16<T, NT, VPL, kPol, FUSED>;
+  CE_CFG_CASES(MAKE)
+#undef MAKE
+  return nullptr;
+}
+template <bool FUSED>
+KernelFn row32_fn(Cfg c) {
+#define MAKE(NT, VPL) \
+  if (c.nt == NT && c.vpl == VPL) return cek::row_kernel_32<NT, VPL, kPol, FUSED>;
+  CE_CFG_CASES(MAKE)
+#undef MAKE
+  return nullptr;
+}
+template <typename T>
+KernelFn stats_fn(Cfg c) {
+#define MAKE(NT, VPL) \
+  if (c.nt == NT && c.vpl == VPL) return cek::slab_stats_kernel<T, NT, VPL, kPol>;
+  CE_CFG_CASES(MAKE)
+#undef MAKE
+  return nullptr;
+}
+template <typename T>
+KernelFn slabgrad_fn(Cfg c) {
+#define MAKE(NT, VPL) \
+  if (c.nt == NT && c.vpl == VPL) return cek::slab_grad_kernel<T, NT, VPL, kPol>;
+  CE_CFG_CASES(MAKE)
+#undef MAKE
+  return nullptr;
+}
+
+constexpr int kGradNT = 256, kGradVPL = 4;  // backward slab: 1024 vectors
+KernelFn grad_fn(int dtype) {
+  if (dtype == CE_DTYPE_BF16) return cek::grad_kernel<cek::BF16, kGradNT, kGradVPL, kPol>;
+  if (dtype == CE_DTYPE_F16) return cek::grad_kernel<cek::F16, kGradNT, kGradVPL, kPol>;
+  return cek::grad_kernel<cek::F32, kGradNT, kGradVPL, kPol>;
+}
+
+KernelFn row_fn(int dtype, bool fused, Cfg c) {
+  if (dtype == CE_DTYPE_BF16) return fused ? row16_fn<cek::BF16, true>(c) : row16_fn<cek::BF16, false>(c);
+  if (dtype == CE_DTYPE_F16) return fused ? row16_fn<cek::F16, true>(c) : row16_fn<cek::F16, false>(c);
+  return fused ? row32_fn<true>(c) : row32_fn<false>(c);
+}
+KernelFn slab_stats_fn(int dtype, Cfg c) {
+  if (dtype == CE_DTYPE_BF16) return stats_fn<cek::BF16>(c);
+  if (dtype == CE_DTYPE_F16) return stats_fn<cek::F16>(c);
+  return stats_fn<cek::F32>(c);
+}
+KernelFn slab_grad_fn(int dtype, Cfg c) {
+  if (dtype == CE_DTYPE_BF16) return slabgrad_fn<cek::BF16>(c);
+  if (dtype == CE_DTYPE_F16) return slabgrad_fn<cek::F16>(c);
+  return nullptr;  // fp32 chunked rows take forward + backward
+}
+
+Args base_args(const void* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V, int64_t ignore,
+               void* ws) {
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.logits = (char*)logits;
+  a.ld = ld;
+  a.grad = (char*)logits;
+  a.grad_ld = ld;
+  a.labels = labels;
+  a.N = N;
+  a.V = V;
+  a.ignore = ignore;
+  a.ws = (cek::WsHeader*)ws;
+  a.C = 1;
+  return a;
+}
+
+// Forward (and, when fused, the in-place gradient) of one call.
+int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V, int dtype,
+                int64_t ignore, int64_t chunk, const float* dloss, float* loss_mean, float* loss_rows,
+                double* lse_rows, double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* ws,
+                size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(logits, ld, labels, N, V, dtype);
+  if (rc != CE_OK) return rc;
+  if (chunk < 0) return CE_ERR_INVALID_ARG;
+  if (loss_mean == nullptr || n_valid == nullptr || (N > 0 && loss_rows == nullptr)) return CE_ERR_INVALID_ARG;
+  Split sp;
+  if (!make_split(V, chunk, dtype, &sp)) return CE_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(N, sp);
+  if (ws == nullptr || ws_bytes < L.total || ((uintptr_t)ws) % 256 != 0) return CE_ERR_WORKSPACE;
+  if (N == 0) {
+    hipLaunchKernelGGL(cek::empty_call_kernel, dim3(1), dim3(64), 0, st, loss_mean, n_valid, status);
+    return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+  }
+  Args a = base_args(logits, ld, labels, N, V, ignore, ws);
+  a.slots = (uint64_t*)((char*)ws + L.slots);
+  a.dloss = dloss;
+  a.loss_mean = loss_mean;
+  a.loss_rows = loss_rows;
+  a.lse_rows = lse_rows;
+  a.pcomp_rows = pcomp_rows;
+  a.n_valid_out = n_valid;
+  a.status = status;
+  const int e = epv(dtype);
+  if (sp.C == 1) {
+    const Cfg c = pick_cfg((V + e - 1) / e);
+    a.K = counters_for(N, N);
+    return launch(row_fn(dtype, fused, c), N, c.nt, a, st);
+  }
+  // chunked: per-slab statistics, then merge (+ gradient)
+  char* wsb = (char*)ws;
+  a.slab_ms = (double2*)(wsb + L.slab_ms);
+  a.slab_xy = (float*)(wsb + L.slab_xy);
+  a.chunk = sp.width;
+  a.C = sp.C;
+  const Cfg c = pick_cfg((sp.width + e - 1) / e);
+  const int64_t G = N * sp.C;
+  a.K = counters_for(N, G);
+  rc = launch(slab_stats_fn(dtype, c), G, c.nt, a, st);
+  if (rc != CE_OK) return rc;
+  if (fused && dtype != CE_DTYPE_F32) return launch(slab_grad_fn(dtype, c), G, c.nt, a, st);
+  if (fused) {  // fp32: row statistics first, then the elementwise backward
+    if (!a.lse_rows) a.lse_rows = (double*)(wsb + L.lse_scratch);
+    if (!a.pcomp_rows) a.pcomp_rows = (double*)(wsb + L.pcomp_scratch);
+  }
+  rc = launch(cek::slab_merge_kernel<64>, N, 64, a, st);
+  if (rc != CE_OK || !fused) return rc;
+  Args b = a;
+  b.lse_in = a.lse_rows;
+  b.pcomp_in = a.pcomp_rows;
+  b.n_valid_in = n_valid;
+  b.C = (int)(((V + e - 1) / e + kGradNT * kGradVPL - 1) / (kGradNT * kGradVPL));
+  return launch(grad_fn(dtype), N * (int64_t)b.C, kGradNT, b, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ce_abi_version(void) { return CE_ABI_VERSION; }
+
+const char* ce_error_string(int code) {
+  switch (code) {
+    case CE_OK: return "ok";
+    case CE_ERR_INVALID_ARG: return "invalid argument (size, stride, pointer or alignment)";
+    case CE_ERR_DTYPE: return "unknown dtype";
+    case CE_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than ce_workspace_bytes()";
+    case CE_ERR_UNSUPPORTED: return "request not served by this build";
+    case CE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+size_t ce_workspace_bytes(int64_t n_rows, int64_t vocab, int64_t chunk, int dtype) {
+  if (!valid_dtype(dtype) || n_rows < 0 || n_rows > kMaxRows || vocab < 1 || vocab > kMaxRows || chunk < 0) return 0;
+  Split sp;
+  if (!make_split(vocab, chunk, dtype, &sp)) return 0;
+  return ws_layout(n_rows, sp).total;
+}
+
+int ce_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr || workspace_bytes < cek::kWsHeaderBytes || ((uintptr_t)workspace) % 256 != 0)
+    return CE_ERR_WORKSPACE;
+  const size_t words = workspace_bytes / 4;
+  int64_t blocks = (int64_t)((words + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(cek::ws_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)workspace, words);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+int ce_forward(const void* logits, int64_t ld, const int64_t* labels, int64_t n_rows, int64_t vocab, int dtype,
+               int64_t ignore_index, int64_t chunk, float* loss_mean, float* loss_rows, double* lse_rows,
+               double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  return run_forward(false, (void*)logits, ld, labels, n_rows, vocab, dtype, ignore_index, chunk, nullptr,
+                     loss_mean, loss_rows, lse_rows, pcomp_rows, n_valid, status, workspace, workspace_bytes,
+                     (hipStream_t)stream);
+}
+
+int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t n_rows, int64_t vocab, int dtype,
+                       int64_t ignore_index, int64_t chunk, const float* dloss, float* loss_mean, float* loss_rows,
+                       double* lse_rows, double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return run_forward(true, logits, ld, labels, n_rows, vocab, dtype, ignore_index, chunk, dloss, loss_mean,
+                     loss_rows, lse_rows, pcomp_rows, n_valid, status, workspace, workspace_bytes,
+                     (hipStream_t)stream);
+}
+
+int ce_backward(const void* logits, int64_t ld, const int64_t* labels, const double* lse_rows,
+                const double* pcomp_rows, const int32_t* n_valid, const float* dloss, int64_t n_rows, int64_t vocab,
+                int dtype, int64_t ignore_index, void* grad, int64_t grad_ld, void* stream) {
+  int rc = check_shape(logits, ld, labels, n_rows, vocab, dtype);
+  if (rc != CE_OK) return rc;
+  if (n_rows == 0) return CE_OK;
+  if (lse_rows == nullptr || pcomp_rows == nullptr || n_valid == nullptr || grad == nullptr || grad_ld < vocab)
+    return CE_ERR_INVALID_ARG;
+  const int es = esize(dtype);
+  if (((uintptr_t)grad) % es != 0) return CE_ERR_INVALID_ARG;
+  const uintptr_t lo = (uintptr_t)logits, go = (uintptr_t)grad;
+  if (go == lo) {
+    if (grad_ld != ld) return CE_ERR_INVALID_ARG;
+  } else {
+    const uintptr_t lend = lo + (uintptr_t)((n_rows - 1) * ld + vocab) * es;
+    const uintptr_t gend = go + (uintptr_t)((n_rows - 1) * grad_ld + vocab) * es;
+    if (go < lend && lo < gend) return CE_ERR_INVALID_ARG;  // partial overlap
+    if ((go & 15) != (lo & 15) || ((grad_ld * es) & 15) != ((ld * es) & 15)) return CE_ERR_UNSUPPORTED;
+  }
+  Args a = base_args(logits, ld, labels, n_rows, vocab, ignore_index, nullptr);
+  a.grad = (char*)grad;
+  a.grad_ld = grad_ld;
+  a.lse_in = lse_rows;
+  a.pcomp_in = pcomp_rows;
+  a.n_valid_in = n_valid;
+  a.dloss = dloss;
+  const int e = epv(dtype);
+  a.C = (int)(((vocab + e - 1) / e + kGradNT * kGradVPL - 1) / (kGradNT * kGradVPL));
+  return launch(grad_fn(dtype), n_rows * (int64_t)a.C, kGradNT, a, (hipStream_t)stream);
+}
+
+}  // extern "C"

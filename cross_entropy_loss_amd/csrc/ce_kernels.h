@@ -1,0 +1,1216 @@
+// ce_kernels.h -- gfx950 device code for token-level softmax cross-entropy.
+//
+// What is computed (per logit row x[0..V) with label y; the pages' "Fast
+// Cross Entropy" kernel, PyPI page "fms-acceleration-foak 0.7.4", kernel
+// list): the softmax cross-entropy loss lse - x_y, its token mean over rows
+// whose label is not ignore_index (fms-hf-tuning PR #280, "Early Version Of
+// This Plugin": per-token averaging), and the gradient
+// (softmax - onehot) * dloss / n_valid.
+//
+// Shape of the work on CDNA4.  The path is a streaming row reduction bound by
+// HBM bandwidth, not a contraction, so there is no MFMA here.  One workgroup
+// owns one row (or one vocabulary slab of a row).  Every lane issues all of
+// its 16-byte loads of the row up front (VPL loads per lane, NT lanes, held
+// in VGPRs: 64 VGPRs for a 64000-byte bf16 row at NT=256), so the row is read
+// from HBM once and the gradient is computed from registers and written once.
+//
+// Numerics for 16-bit inputs (fp32 arithmetic, v_exp_f32 on base 2):
+//   pass 0  per-lane max m_l (bf16: also a lower bound of the lane minimum)
+//   pass 1  per-lane s_l = sum_{j != y} 2^{(x_j - m_l) log2 e}; the label
+//           element is set to -inf in registers first, so the sum excludes it
+//           without a subtraction
+//   merge   (m, s) pairs across the workgroup -> M, S_excl
+//   row     e_y = exp(x_y - M), S = S_excl + e_y, lse = M + log S,
+//           q = S_excl / S  (= 1 - p_y, no cancellation)
+//           loss = lse - x_y when q >= 1/2, else log1p(S_excl / e_y)
+//   pass 2  g_j = 2^{(x_j - lse) log2 e} * s  (s = dloss / n_valid),
+//           g_y = -s q, rounded once to the storage format (nearest-even).
+// fp32 inputs run the same steps in fp64 and round once to fp32.
+//
+// The valid-token count.  The gradient scale needs n_valid of the whole
+// batch before any row is written.  The first K workgroups of the launch
+// each count a slice of the labels and publish an epoch-tagged partial count
+// (one 64-bit relaxed agent-scope atomic store: tag << 32 | bad << 31 |
+// count); every row polls the K words with a bounded wait.  Workgroups are
+// dispatched in increasing id order on each XCD, so the K counters are
+// resident before any poller can fill the machine; the wait is bounded
+// anyway (CE_STATUS_SYNC_TIMEOUT) so a wave never spins forever.
+//
+// The mean.  Each row publishes its loss into its own epoch-tagged 64-bit
+// slot of the workspace (tag << 32 | loss bits: one relaxed agent-scope
+// store, so no fence and no shared counter).  The last workgroup of the grid
+// polls the N slots, sums the losses in row order in fp64 (deterministic),
+// writes L, n_valid and the status word, then bumps the epoch so the
+// workspace is ready for the next call.  No workgroup ever waits for the
+// finisher, so the wait cannot deadlock.  (Same-address device-scope atomics,
+// one per workgroup, serialise at the memory side at tens of ns each, and an
+// agent-scope release writes back the whole L2: both cost more than the
+// kernel itself at these sizes.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cek {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kStatusLabelRange = 0x1u;
+constexpr uint32_t kStatusSyncTimeout = 0x2u;
+constexpr int kMaxCounters = 64;
+constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus s_sleep): ~0.5 s
+
+// ---------------------------------------------------------------------------
+// Workspace header (device memory owned by the caller, zero-filled once).
+// ---------------------------------------------------------------------------
+struct WsHeader {
+  uint32_t epoch;  // bumped by the finishing workgroup of every call
+  uint32_t flags;  // status bits raised by workgroups of the running call
+  uint32_t pad0[14];
+  uint64_t part[kMaxCounters];  // tagged partial label counts
+};
+constexpr size_t kWsHeaderBytes = 1024;
+static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header too large");
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reinterpret one 32-bit lane word.  The word is taken by value: clang's
+// __builtin_bit_cast applied directly to an ext-vector element expression
+// (v[i]) reads element 0 whatever i is, so element accesses never go into a
+// bit cast directly.
+template <typename T>
+__device__ __forceinline__ T as(uint32_t w) {
+  return __builtin_bit_cast(T, w);
+}
+
+// ---------------------------------------------------------------------------
+// Element formats.  A 16-byte vector holds EPV elements.
+// ---------------------------------------------------------------------------
+struct BF16 {
+  static constexpr int ESZ = 2, EPV = 8;
+  static constexpr bool kBF = true;
+  typedef uint16_t bits_t;
+  typedef float acc_t;
+  // smallest |scale| at which a flushed 2^t (t < -126) could change a rounded
+  // output: scale * 2^-126 reaches half of the smallest subnormal 2^-133
+  static constexpr float kSlowScale = 0x1p-8f;
+  __device__ static float lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+  __device__ static float hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+  __device__ static float load1(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+  __device__ static uint32_t pack(float a, float b) {
+    f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+  }
+  __device__ static uint16_t store1(float a) { return (uint16_t)(pack(a, 0.0f) & 0xffffu); }
+  __device__ static void kill(u32x4& v, int e) {  // element e := -inf
+    const uint32_t mask = (e & 1) ? 0xffff0000u : 0x0000ffffu;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (d == (e >> 1)) v[d] = (v[d] & ~mask) | (0xff80ff80u & mask);
+  }
+};
+
+struct F16 {
+  static constexpr int ESZ = 2, EPV = 8;
+  static constexpr bool kBF = false;
+  typedef uint16_t bits_t;
+  typedef float acc_t;
+  // fp16's smallest subnormal is 2^-24, so flushed 2^t below 2^-126 matter
+  // only for |scale| above 2^101
+  static constexpr float kSlowScale = 0x1p101f;
+  __device__ static float lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u).x; }
+  __device__ static float hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u).y; }
+  __device__ static float load1(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+  __device__ static uint32_t pack(float a, float b) {
+    f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  }
+  __device__ static uint16_t store1(float a) { return (uint16_t)(pack(a, 0.0f) & 0xffffu); }
+  __device__ static void kill(u32x4& v, int e) {
+    const uint32_t mask = (e & 1) ? 0xffff0000u : 0x0000ffffu;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (d == (e >> 1)) v[d] = (v[d] & ~mask) | (0xfc00fc00u & mask);
+  }
+};
+
+struct F32 {
+  static constexpr int ESZ = 4, EPV = 4;
+  typedef uint32_t bits_t;
+  typedef double acc_t;
+  __device__ static float load1(uint32_t b) { return __builtin_bit_cast(float, b); }
+  __device__ static uint32_t store1(float a) { return __builtin_bit_cast(uint32_t, a); }
+  __device__ static void kill(u32x4& v, int e) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (d == e) v[d] = 0xff800000u;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cache policy of the streaming loads and stores (bit 0: nontemporal loads,
+// bit 1: nontemporal stores).
+// ---------------------------------------------------------------------------
+template <int POL>
+__device__ __forceinline__ u32x4 ldv(const u32x4* p) {
+  if constexpr (POL & 1) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <int POL>
+__device__ __forceinline__ void stv(u32x4* p, u32x4 v) {
+  if constexpr (POL & 2) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions.
+// ---------------------------------------------------------------------------
+template <typename F>
+__device__ __forceinline__ F wave_sum(F v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Merge of two (max, sum-relative-to-max) pairs; a pair with m = -inf is empty.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  const float a = (m == -INFINITY) ? 0.0f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  const float b = (m2 == -INFINITY) ? 0.0f : s2 * __builtin_amdgcn_exp2f((m2 - M) * kLog2e);
+  m = M;
+  s = a + b;
+}
+__device__ __forceinline__ void ms_merge(double& m, double& s, double m2, double s2) {
+  const double M = fmax(m, m2);
+  const double a = (m == -INFINITY) ? 0.0 : s * exp(m - M);
+  const double b = (m2 == -INFINITY) ? 0.0 : s2 * exp(m2 - M);
+  m = M;
+  s = a + b;
+}
+template <typename F>
+__device__ __forceinline__ void wave_ms(F& m, F& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const F m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-call arguments.
+// ---------------------------------------------------------------------------
+struct Args {
+  char* logits;  // row i at logits + i * ld * ESZ
+  int64_t ld;    // row stride in elements
+  char* grad;    // gradient rows (== logits for in-place)
+  int64_t grad_ld;
+  const int64_t* labels;
+  int64_t N, V, ignore;
+  const float* dloss;  // NULL = 1
+  float* loss_mean;
+  float* loss_rows;
+  double* lse_rows;    // nullable
+  double* pcomp_rows;  // nullable
+  int32_t* n_valid_out;
+  const int32_t* n_valid_in;  // backward
+  const double* lse_in;       // backward
+  const double* pcomp_in;     // backward
+  uint32_t* status;           // nullable
+  WsHeader* ws;
+  uint64_t* slots;   // [N] tagged per-row losses for the finisher
+  double2* slab_ms;  // [N * C] (max, label-excluded sum) per vocabulary slab
+  float* slab_xy;    // [N] label logit, written by the slab that holds it
+  int64_t chunk;     // slab width in elements (chunked kernels)
+  int C;             // slabs per row
+  int K;             // counter workgroups
+};
+
+// Geometry of V elements starting at `base`: `head` elements before the first
+// 16-byte boundary, `nvec` aligned 16-byte vectors, then `tail` elements.
+struct Geom {
+  int head, tail, nvec;
+};
+template <int ESZ, int EPV>
+__device__ __forceinline__ Geom geom(const char* base, int64_t V) {
+  Geom g;
+  const uintptr_t a = (uintptr_t)base;
+  int64_t h = (int64_t)(((16 - (a & 15)) & 15) / ESZ);
+  if (h > V) h = V;
+  g.head = (int)h;
+  g.nvec = (int)((V - h) / EPV);
+  g.tail = (int)((V - h) % EPV);
+  return g;
+}
+
+// Where element j (0 <= j < V, or -1 for none) of a geometry lives, as seen by
+// lane `tid` of NT: in this lane's head slot, tail slot, or body vector k,
+// element e.  Fields are -1 when this lane does not hold it.
+struct Owner {
+  int head, tail, k, e;
+};
+template <int NT, int EPV>
+__device__ __forceinline__ Owner owner(const Geom& g, int64_t j, int tid) {
+  Owner o = {-1, -1, -1, 0};
+  if (j < 0) return o;
+  if (j < g.head) {
+    if (tid == (int)j) o.head = 1;
+  } else if (j - g.head < (int64_t)g.nvec * EPV) {
+    const int vy = (int)((j - g.head) / EPV);
+    if (tid == vy % NT) {
+      o.k = vy / NT;
+      o.e = (int)((j - g.head) % EPV);
+    }
+  } else if (tid == (int)(j - g.head - (int64_t)g.nvec * EPV)) {
+    o.tail = 1;
+  }
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Label counting, the poll, loss publication and the call's finish.
+// ---------------------------------------------------------------------------
+// Counter workgroup j of K counts labels [N*j/K, N*(j+1)/K) and publishes.
+template <int NT>
+__device__ void count_and_publish(const Args& a, int j, uint32_t tag, uint32_t* lds_u32) {
+  const int tid = threadIdx.x;
+  const int64_t i0 = a.N * j / a.K, i1 = a.N * (j + 1) / a.K;
+  uint32_t cnt = 0, bad = 0;
+  for (int64_t i = i0 + tid; i < i1; i += NT) {
+    const int64_t y = a.labels[i];
+    if (y != a.ignore) {
+      cnt += 1;
+      bad |= (y < 0 || y >= a.V) ? 1u : 0u;
+    }
+  }
+  cnt = wave_sum(cnt);
+  bad = wave_or(bad);
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
+    lds_u32[2 * w] = cnt;
+    lds_u32[2 * w + 1] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t c = 0, b = 0;
+    for (int k = 0; k < NT / 64; ++k) {
+      c += lds_u32[2 * k];
+      b |= lds_u32[2 * k + 1];
+    }
+    st_agent(&a.ws->part[j], ((uint64_t)tag << 32) | ((uint64_t)(b & 1u) << 31) | (uint64_t)(c & 0x7fffffffu));
+  }
+  __syncthreads();
+}
+
+// Raises a status bit (rare error paths only) and waits until it has landed,
+// so that it is visible before this workgroup publishes its row.
+__device__ __forceinline__ void raise_flag(const Args& a, uint32_t bit) {
+  __hip_atomic_fetch_or(&a.ws->flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wave 0 polls the K partial counts and leaves n_valid and the bad-label bit
+// in lds_u[0], lds_u[1] (read them after a barrier).
+__device__ void poll_to_lds(const Args& a, uint32_t tag, uint32_t* lds_u) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  uint64_t w = 0;
+  uint32_t to = 0;
+  if (lane < a.K) {
+    for (int it = 0;; ++it) {
+      w = ld_agent(&a.ws->part[lane]);
+      if ((uint32_t)(w >> 32) == tag) break;
+      if (it >= kSpinLimit) {
+        to = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  uint32_t c = (lane < a.K) ? (uint32_t)(w & 0x7fffffffu) : 0u;
+  uint32_t b = (lane < a.K) ? (uint32_t)((w >> 31) & 1u) : 0u;
+  c = wave_sum(c);
+  b = wave_or(b);
+  to = wave_or(to);
+  if (lane == 0) {
+    lds_u[0] = c;
+    lds_u[1] = b;
+    if (to) raise_flag(a, kStatusSyncTimeout);
+  }
+}
+
+// A row's loss, published for the finisher (one thread).
+__device__ __forceinline__ void publish_loss(const Args& a, int64_t row, float loss, uint32_t tag) {
+  st_agent(&a.slots[row], ((uint64_t)tag << 32) | (uint64_t)__builtin_bit_cast(uint32_t, loss));
+}
+
+// Run by the last workgroup of the grid, after its own row: waits for every
+// row's tagged loss, sums in row order (fp64), writes L, n_valid and status,
+// and bumps the epoch.  n and bad come from this workgroup's poll.
+template <int NT>
+__device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t bad, double* lds_d) {
+  const int tid = threadIdx.x;
+  const uint32_t tag = epoch + 1u;
+  constexpr int B = 8;  // slot loads in flight per lane
+  double acc = 0.0;
+  uint32_t to = 0;
+  for (int64_t base = 0; base < a.N; base += (int64_t)NT * B) {
+    uint64_t w[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      if (i < a.N) w[j] = ld_agent(&a.slots[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      if (i < a.N) {
+        for (int it = 0; (uint32_t)(w[j] >> 32) != tag; ++it) {
+          if (it >= kSpinLimit) {
+            to = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          w[j] = ld_agent(&a.slots[i]);
+        }
+        acc += (double)__builtin_bit_cast(float, (uint32_t)(w[j] & 0xffffffffu));
+      }
+    }
+  }
+  lds_d[tid] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int s = NT / 2; s >= 1; s >>= 1) {
+    if (tid < s) lds_d[tid] += lds_d[tid + s];
+    __syncthreads();
+  }
+  const int any_to = __syncthreads_or((int)to);
+  if (tid == 0) {
+    const uint32_t flags = ld_agent(&a.ws->flags) | (any_to ? kStatusSyncTimeout : 0u);
+    a.loss_mean[0] = (float)(lds_d[0] / (double)n);
+    a.n_valid_out[0] = (int32_t)n;
+    if (a.status) a.status[0] = (bad ? kStatusLabelRange : 0u) | flags;
+    st_agent(&a.ws->flags, 0u);
+    st_agent(&a.ws->epoch, epoch + 1u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lane passes over the staged vectors (16-bit formats, fp32 arithmetic).
+// ---------------------------------------------------------------------------
+// pass 0: lane max; for bf16 also a lower bound of the lane min.  The bf16
+// high element is read as the whole dword (its low half becomes extra
+// mantissa bits), which moves it by less than one bf16 ulp -- harmless for a
+// max used only as the stabilising shift.
+template <typename T, int NT, int VPL>
+__device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int tid, float& m, float& mn) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    if (k * NT + tid < nvec) {
+      if constexpr (T::kBF) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t u = v[k][d];
+          const float a0 = __builtin_bit_cast(float, u), a1 = __builtin_bit_cast(float, u << 16);
+          m = fmaxf(m, fmaxf(a0, a1));
+          mn = fminf(mn, fminf(a0, a1));
+        }
+      } else {
+        h2 hm = as<h2>(v[k][0]);
+#pragma unroll
+        for (int d = 1; d < 4; ++d) hm = __builtin_elementwise_max(hm, as<h2>(v[k][d]));
+        m = fmaxf(m, fmaxf((float)hm.x, (float)hm.y));
+      }
+    }
+  }
+}
+
+// pass 1: sum of 2^{x log2 e - mc} over the lane's elements.
+template <typename T, int NT, int VPL>
+__device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int tid, float mc, float xh, float xt) {
+  float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xh, kLog2e, -mc));
+  float s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -mc));
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    if (k * NT + tid < nvec) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t u = v[k][d];
+        s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(T::lo(u), kLog2e, -mc));
+        s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(T::hi(u), kLog2e, -mc));
+      }
+    }
+  }
+  return s0 + s1;
+}
+
+// One gradient element of a 16-bit row.  MODE selects the arithmetic:
+//   kFold  g = 2^(x log2e - b), b = lse log2e - log2 s   (s > 0 and finite)
+//   kMul   g = 2^(x log2e - lse log2e) * s               (any s)
+//   kF64   g = exp(x - lse) * s in fp64                  (outputs that may be
+//          subnormal in bf16, where v_exp_f32 would flush below 2^-126)
+enum { kFold = 0, kMul = 1, kF64 = 2 };
+struct GradConsts {
+  float b;        // kFold exponent offset
+  float lc;       // lse * log2e
+  float scale;    // s
+  double lse_d;   // lse (fp64 path)
+  double scale_d; // s (fp64 path)
+  float gy;       // the label element's gradient, -s (1 - p_y)
+};
+template <int MODE>
+__device__ __forceinline__ float gelem(float x, const GradConsts& k) {
+  if constexpr (MODE == kFold) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.b));
+  else if constexpr (MODE == kMul) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.lc)) * k.scale;
+  else return (float)(exp((double)x - k.lse_d) * k.scale_d);
+}
+
+// pass 2: gradient of the staged vectors, stored to gbody.  The label element
+// (held by lane/vector `own`) gets k.gy.
+template <typename T, int NT, int VPL, int POL, int MODE>
+__device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
+                                         const Owner& own) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = k * NT + tid;
+    if (idx < nvec) {
+      float gv[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        gv[2 * d] = gelem<MODE>(T::lo(v[k][d]), kc);
+        gv[2 * d + 1] = gelem<MODE>(T::hi(v[k][d]), kc);
+      }
+      if (k == own.k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = (e == own.e) ? kc.gy : gv[e];
+      }
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
+      stv<POL>(gbody + idx, o);
+    }
+  }
+}
+
+// Head / tail elements of a 16-bit row (one per lane at most).
+template <typename T, int MODE>
+__device__ __forceinline__ float gscalar(float x, bool is_label, const GradConsts& kc) {
+  return is_label ? kc.gy : gelem<MODE>(x, kc);
+}
+
+// Picks the pass-2 arithmetic for a row.  tmin: a lower bound of
+// min_j (x_j - lse) log2e over the row (only used for bf16).
+template <typename T>
+__device__ __forceinline__ int grad_mode(float scale, float tmin) {
+  const bool pos = scale > 0.0f && scale <= 3.0e38f;
+  if (pos) {
+    // folded: 2^t with t = (x - lse) log2e + log2 s is flushed below 2^-126,
+    // which matters only for bf16 (its subnormals reach 2^-133)
+    if (T::kBF && tmin + log2f(scale) < -125.0f) return kF64;
+    return kFold;
+  }
+  if (fabsf(scale) > T::kSlowScale && (!T::kBF || tmin < -125.0f)) return kF64;
+  return kMul;
+}
+
+template <typename T>
+__device__ __forceinline__ GradConsts grad_consts(float lse, float scale, double scale_d, double pcomp) {
+  GradConsts k;
+  k.lc = lse * kLog2e;
+  k.b = k.lc - log2f(scale);  // used only when scale > 0
+  k.scale = scale;
+  k.lse_d = (double)lse;
+  k.scale_d = scale_d;
+  k.gy = (float)(-scale_d * pcomp);
+  return k;
+}
+
+// Writes NaN over a row whose label is out of range.
+template <typename T, int NT, int VPL, int POL>
+__device__ __forceinline__ void nan_row(char* gbase, const Geom& g, int tid, int v0) {
+  u32x4* gbody = (u32x4*)(gbase + g.head * T::ESZ);
+  const uint32_t q = (T::ESZ == 2) ? 0x7fc07fc0u : 0x7fc00000u;
+  const u32x4 z = {q, q, q, q};
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = v0 + k * NT + tid;
+    if (idx < g.nvec) stv<POL>(gbody + idx, z);
+  }
+  if (v0 == 0) {
+    typedef typename T::bits_t B;
+    if (tid < g.head) ((B*)gbase)[tid] = (B)q;
+    if (tid < g.tail) ((B*)gbase)[g.head + (int64_t)g.nvec * T::EPV + tid] = (B)q;
+  }
+}
+
+// Whole pass 2 of a 16-bit row (or slab): nvec staged body vectors written
+// to gbody, plus this lane's head element (to *ph) and tail element (to *pt)
+// when it has them.
+template <typename T, int NT, int VPL, int POL>
+__device__ __forceinline__ void grad_row_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, int mode,
+                                            const GradConsts& kc, const Owner& own, float xh, float xt,
+                                            typename T::bits_t* ph, typename T::bits_t* pt) {
+  float gh = 0.0f, gt = 0.0f;
+  if (mode == kFold) {
+    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own);
+    gh = gscalar<T, kFold>(xh, own.head > 0, kc);
+    gt = gscalar<T, kFold>(xt, own.tail > 0, kc);
+  } else if (mode == kMul) {
+    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own);
+    gh = gscalar<T, kMul>(xh, own.head > 0, kc);
+    gt = gscalar<T, kMul>(xt, own.tail > 0, kc);
+  } else {
+    pass2_16<T, NT, VPL, POL, kF64>(v, nvec, tid, gbody, kc, own);
+    gh = gscalar<T, kF64>(xh, own.head > 0, kc);
+    gt = gscalar<T, kF64>(xt, own.tail > 0, kc);
+  }
+  if (ph) *ph = T::store1(gh);
+  if (pt) *pt = T::store1(gt);
+}
+
+// Lane minimum of 16-bit staged vectors (bf16 only; a lower bound within one
+// bf16 ulp, as in pass 0).
+template <typename T, int NT, int VPL>
+__device__ __forceinline__ float lane_min_16(const u32x4 (&v)[VPL], int nvec, int tid, float mn) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k)
+    if (k * NT + tid < nvec)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t u = v[k][d];
+        mn = fminf(mn, fminf(__builtin_bit_cast(float, u), __builtin_bit_cast(float, u << 16)));
+      }
+  return mn;
+}
+
+// grad_mode for a workgroup whose lanes each know only their own minimum:
+// the fp64 fallback is agreed with one barrier (bf16 only).
+template <typename T>
+__device__ __forceinline__ int block_grad_mode(float scale, float tmin_lane) {
+  const bool pos = scale > 0.0f && scale <= 3.0e38f;
+  if constexpr (T::kBF) {
+    const bool lane = pos ? (tmin_lane + log2f(scale) < -125.0f) : (fabsf(scale) > T::kSlowScale && tmin_lane < -125.0f);
+    if (__syncthreads_or(lane ? 1 : 0)) return kF64;
+    return pos ? kFold : kMul;
+  } else {
+    if (pos) return kFold;
+    return fabsf(scale) > T::kSlowScale ? kF64 : kMul;
+  }
+}
+
+// Writes +0 over the row's elements (ignored rows are not read).
+template <typename T, int NT, int VPL, int POL>
+__device__ __forceinline__ void zero_row(char* gbase, const Geom& g, int tid, int v0) {
+  u32x4* gbody = (u32x4*)(gbase + g.head * T::ESZ);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = v0 + k * NT + tid;
+    if (idx < g.nvec) stv<POL>(gbody + idx, z);
+  }
+  if (v0 == 0) {
+    typedef typename T::bits_t B;
+    if (tid < g.head) ((B*)gbase)[tid] = 0;
+    if (tid < g.tail) ((B*)gbase)[g.head + (int64_t)g.nvec * T::EPV + tid] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-row kernel for 16-bit formats (bf16, fp16).
+//   FUSED: forward + gradient written over the row.   !FUSED: forward only.
+// One workgroup of NT lanes per row; row capacity NT * VPL vectors.
+// ---------------------------------------------------------------------------
+template <typename T, int NT, int VPL, int POL, bool FUSED>
+__global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
+  constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
+  __shared__ float lds_m[NW], lds_s[NW], lds_mn[NW];
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  __shared__ double lds_d[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t row = blockIdx.x;
+
+  const uint32_t epoch = ld_agent(&a.ws->epoch);  // unchanged until the finisher's last store
+  const uint32_t tag = epoch + 1u;
+  if (row < a.K) count_and_publish<NT>(a, (int)row, tag, lds_u + 4);
+
+  char* rbase = a.logits + row * a.ld * ESZ;
+  const int64_t y = a.labels[row];
+  const bool ignored = (y == a.ignore);
+  const bool badlab = !ignored && (y < 0 || y >= a.V);
+  const Geom g = geom<ESZ, EPV>(rbase, a.V);
+  const u32x4* body = (const u32x4*)(rbase + g.head * ESZ);
+  typedef typename T::bits_t B;
+
+  // ---- issue every load of the row -------------------------------------
+  u32x4 v[VPL];
+  float xh = -INFINITY, xt = -INFINITY;  // this lane's head / tail element
+  const bool has_h = tid < g.head, has_t = tid < g.tail;
+  if (!ignored) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = k * NT + tid;
+      if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
+    }
+    if (has_h) xh = T::load1(((const B*)rbase)[tid]);
+    if (has_t) xt = T::load1(((const B*)rbase)[g.head + (int64_t)g.nvec * EPV + tid]);
+  }
+  const float xy = (!ignored && !badlab) ? T::load1(((const B*)rbase)[y]) : 0.0f;
+  poll_to_lds(a, tag, lds_u);
+
+  float lse = 0.0f, loss = 0.0f, pcomp = 0.0f;
+  if (!ignored) {
+    float m = fmaxf(xh, xt);
+    float mn = INFINITY;
+    if (has_h) mn = xh;
+    if (has_t) mn = fminf(mn, xt);
+    pass0_16<T, NT, VPL>(v, g.nvec, tid, m, mn);
+    const Owner own = owner<NT, EPV>(g, badlab ? -1 : y, tid);
+    if (own.head > 0) xh = -INFINITY;
+    if (own.tail > 0) xt = -INFINITY;
+    if (own.k >= 0) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        if (k == own.k) T::kill(v[k], own.e);
+    }
+    const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
+    float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh, xt);
+    wave_ms(m, s);
+    mn = wave_min(mn);
+    if (lane == 0) {
+      lds_m[wid] = m;
+      lds_s[wid] = s;
+      lds_mn[wid] = mn;
+    }
+    __syncthreads();
+    float M = lds_m[0], S_ex = lds_s[0], MN = lds_mn[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      ms_merge(M, S_ex, lds_m[w], lds_s[w]);
+      MN = fminf(MN, lds_mn[w]);
+    }
+    if (badlab) {
+      lse = loss = pcomp = __builtin_nanf("");
+    } else {
+      const float ey = __builtin_amdgcn_exp2f((xy - M) * kLog2e);
+      const float S = S_ex + ey;
+      lse = M + logf(S);
+      pcomp = S_ex / S;
+      loss = (pcomp >= 0.5f) ? (lse - xy) : log1pf(S_ex / ey);
+    }
+    if constexpr (FUSED) {
+      char* gbase = a.grad + row * a.grad_ld * ESZ;
+      if (badlab) {
+        nan_row<T, NT, VPL, POL>(gbase, g, tid, 0);
+      } else {
+        const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+        const float scale = (float)scale_d;
+        const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
+        // lower bound of (x - lse) log2e over the row (bf16 lane minima are
+        // lower bounds within one bf16 ulp; widen by 2^-7 relative)
+        const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
+        typedef typename T::bits_t B;
+        grad_row_16<T, NT, VPL, POL>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), grad_mode<T>(scale, tmin), kc,
+                                     own, xh, xt, has_h ? (B*)gbase + tid : nullptr,
+                                     has_t ? (B*)gbase + g.head + (int64_t)g.nvec * EPV + tid : nullptr);
+      }
+    }
+  } else {
+    if constexpr (FUSED) zero_row<T, NT, VPL, POL>(a.grad + row * a.grad_ld * ESZ, g, tid, 0);
+  }
+  if (tid == 0) {
+    a.loss_rows[row] = loss;
+    if (a.lse_rows) a.lse_rows[row] = (double)lse;
+    if (a.pcomp_rows) a.pcomp_rows[row] = (double)pcomp;
+    publish_loss(a, row, loss, tag);
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    __syncthreads();
+    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-row kernel for fp32 inputs: the same steps in fp64, rounded once.
+// ---------------------------------------------------------------------------
+template <int NT, int VPL, int POL, bool FUSED>
+__global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
+  constexpr int ESZ = 4, EPV = 4, NW = NT / 64;
+  __shared__ double lds_m[NW], lds_s[NW];
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  __shared__ double lds_d[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint32_t epoch = ld_agent(&a.ws->epoch);
+  const uint32_t tag = epoch + 1u;
+  if (row < a.K) count_and_publish<NT>(a, (int)row, tag, lds_u + 4);
+
+  char* rbase = a.logits + row * a.ld * ESZ;
+  const int64_t y = a.labels[row];
+  const bool ignored = (y == a.ignore);
+  const bool badlab = !ignored && (y < 0 || y >= a.V);
+  const Geom g = geom<ESZ, EPV>(rbase, a.V);
+  const u32x4* body = (const u32x4*)(rbase + g.head * ESZ);
+  u32x4 v[VPL];
+  float xh = -INFINITY, xt = -INFINITY;
+  const bool has_h = tid < g.head, has_t = tid < g.tail;
+  if (!ignored) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = k * NT + tid;
+      if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
+    }
+    if (has_h) xh = ((const float*)rbase)[tid];
+    if (has_t) xt = ((const float*)rbase)[g.head + (int64_t)g.nvec * EPV + tid];
+  }
+  const double xy = (!ignored && !badlab) ? (double)((const float*)rbase)[y] : 0.0;
+  poll_to_lds(a, tag, lds_u);
+
+  double lse = 0.0, loss = 0.0, pcomp = 0.0;
+  if (!ignored) {
+    float mf = fmaxf(xh, xt);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if (k * NT + tid < g.nvec)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mf = fmaxf(mf, as<float>(v[k][d]));
+    const Owner own = owner<NT, EPV>(g, badlab ? -1 : y, tid);
+    if (own.head > 0) xh = -INFINITY;
+    if (own.tail > 0) xt = -INFINITY;
+    if (own.k >= 0) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        if (k == own.k) F32::kill(v[k], own.e);
+    }
+    double m = (double)mf;
+    const double mm = (mf == -INFINITY) ? 0.0 : m;
+    double s = exp((double)xh - mm) + exp((double)xt - mm);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if (k * NT + tid < g.nvec)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s += exp((double)as<float>(v[k][d]) - mm);
+    wave_ms(m, s);
+    if (lane == 0) {
+      lds_m[wid] = m;
+      lds_s[wid] = s;
+    }
+    __syncthreads();
+    double M = lds_m[0], S_ex = lds_s[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) ms_merge(M, S_ex, lds_m[w], lds_s[w]);
+    if (badlab) {
+      lse = loss = pcomp = __builtin_nan("");
+    } else {
+      const double ey = exp(xy - M);
+      const double S = S_ex + ey;
+      lse = M + log(S);
+      pcomp = S_ex / S;
+      loss = (pcomp >= 0.5) ? (lse - xy) : log1p(S_ex / ey);
+    }
+    if constexpr (FUSED) {
+      const uint32_t n = lds_u[0];
+      const double scale = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)n;
+      char* gbase = a.grad + row * a.grad_ld * ESZ;
+      u32x4* gbody = (u32x4*)(gbase + g.head * ESZ);
+      const double gy = -scale * pcomp;
+      const float nanv = __builtin_nanf("");
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        const int idx = k * NT + tid;
+        if (idx < g.nvec) {
+          u32x4 o;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            double gd = exp((double)as<float>(v[k][d]) - lse) * scale;
+            if (k == own.k && d == own.e) gd = gy;
+            o[d] = __builtin_bit_cast(uint32_t, badlab ? nanv : (float)gd);
+          }
+          stv<POL>(gbody + idx, o);
+        }
+      }
+      if (has_h) {
+        double gh = exp((double)xh - lse) * scale;
+        if (own.head > 0) gh = gy;
+        ((float*)gbase)[tid] = badlab ? nanv : (float)gh;
+      }
+      if (has_t) {
+        double gt = exp((double)xt - lse) * scale;
+        if (own.tail > 0) gt = gy;
+        ((float*)gbase)[g.head + (int64_t)g.nvec * EPV + tid] = badlab ? nanv : (float)gt;
+      }
+    }
+  } else {
+    if constexpr (FUSED) zero_row<F32, NT, VPL, POL>(a.grad + row * a.grad_ld * ESZ, g, tid, 0);
+  }
+  if (tid == 0) {
+    a.loss_rows[row] = (float)loss;
+    if (a.lse_rows) a.lse_rows[row] = lse;
+    if (a.pcomp_rows) a.pcomp_rows[row] = pcomp;
+    publish_loss(a, row, (float)loss, tag);
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    __syncthreads();
+    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward from saved statistics, elementwise:
+//   grad_j = s 2^{(x_j - lse) log2 e} (j != y),  grad_y = -s pcomp,  s = dloss/n.
+// blockIdx.x = row * C + slab, a slab being NT*VPL vectors of the row.  16-bit
+// rows take fp64 exponentials only when |s| is large enough for a flushed
+// 2^t to change a rounded output; fp32 rows always compute in fp64.
+// ---------------------------------------------------------------------------
+template <typename T, int NT, int VPL, int POL>
+__global__ __launch_bounds__(NT) void grad_kernel(Args a) {
+  constexpr int ESZ = T::ESZ, EPV = T::EPV;
+  typedef typename T::bits_t B;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / a.C;
+  const int slab = (int)(blockIdx.x % a.C);
+  const int v0 = slab * NT * VPL;
+  const char* rbase = a.logits + row * a.ld * ESZ;
+  char* gbase = a.grad + row * a.grad_ld * ESZ;
+  const Geom g = geom<ESZ, EPV>(rbase, a.V);
+  const u32x4* body = (const u32x4*)(rbase + g.head * ESZ);
+  u32x4* gbody = (u32x4*)(gbase + g.head * ESZ);
+  const int64_t y = a.labels[row];
+  if (y == a.ignore) {
+    zero_row<T, NT, VPL, POL>(gbase, g, tid, v0);
+    return;
+  }
+  const bool badlab = (y < 0 || y >= a.V);
+  if (badlab) {
+    nan_row<T, NT, VPL, POL>(gbase, g, tid, v0);
+    return;
+  }
+  const double lse_d = a.lse_in[row];
+  const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)a.n_valid_in[0];
+  const double gy_d = -scale_d * a.pcomp_in[row];
+  u32x4 v[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = v0 + k * NT + tid;
+    if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
+  }
+  if constexpr (ESZ == 2) {
+    const bool hh = slab == 0 && tid < g.head, ht = slab == 0 && tid < g.tail;
+    const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
+    const float xh = hh ? T::load1(((const B*)rbase)[tid]) : 0.0f;
+    const float xt = ht ? T::load1(((const B*)rbase)[jt]) : 0.0f;
+    const float scale = (float)scale_d, lse = (float)lse_d;
+    float tmin = INFINITY;
+    if constexpr (T::kBF) {
+      float mn = lane_min_16<T, NT, VPL>(v, g.nvec - v0, tid, INFINITY);
+      if (hh) mn = fminf(mn, xh);
+      if (ht) mn = fminf(mn, xt);
+      tmin = (mn - fabsf(mn) * 0x1p-7f - lse) * kLog2e;
+    }
+    const int mode = block_grad_mode<T>(scale, tmin);
+    const GradConsts kc = grad_consts<T>(lse, scale, scale_d, a.pcomp_in[row]);
+    Owner own = owner<NT, EPV>(g, y, tid);
+    if (own.k >= 0) own.k -= slab * VPL;  // vector index within this slab
+    if (own.k >= VPL) own.k = -1;
+    grad_row_16<T, NT, VPL, POL>(v, g.nvec - v0, tid, gbody + v0, mode, kc, own, xh, xt,
+                                 hh ? (B*)gbase + tid : nullptr, ht ? (B*)gbase + jt : nullptr);
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = v0 + k * NT + tid;
+      if (idx < g.nvec) {
+        const int64_t j0 = g.head + (int64_t)idx * EPV;
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          double gd = exp((double)as<float>(v[k][d]) - lse_d) * scale_d;
+          if (j0 + d == y) gd = gy_d;
+          o[d] = __builtin_bit_cast(uint32_t, (float)gd);
+        }
+        stv<POL>(gbody + idx, o);
+      }
+    }
+    if (slab == 0) {
+      if (tid < g.head) {
+        double gh = exp((double)((const float*)rbase)[tid] - lse_d) * scale_d;
+        if ((int64_t)tid == y) gh = gy_d;
+        ((float*)gbase)[tid] = (float)gh;
+      }
+      if (tid < g.tail) {
+        const int64_t j = g.head + (int64_t)g.nvec * EPV + tid;
+        double gt = exp((double)((const float*)rbase)[j] - lse_d) * scale_d;
+        if (j == y) gt = gy_d;
+        ((float*)gbase)[j] = (float)gt;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked forward, step 1: per (row, vocabulary slab) max and label-excluded
+// sum.  blockIdx.x = row * C + c; slab c covers elements [c*chunk, ...).
+// ---------------------------------------------------------------------------
+template <typename T, int NT, int VPL, int POL>
+__global__ __launch_bounds__(NT) void slab_stats_kernel(Args a) {
+  constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
+  typedef typename T::acc_t A;
+  typedef typename T::bits_t B;
+  __shared__ A lds_m[NW], lds_s[NW];
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t bid = blockIdx.x;
+  const int64_t row = bid / a.C;
+  const int c = (int)(bid % a.C);
+  const uint32_t tag = ld_agent(&a.ws->epoch) + 1u;
+  if (bid < a.K) count_and_publish<NT>(a, (int)bid, tag, lds_u + 4);
+  const int64_t j0 = (int64_t)c * a.chunk;
+  const int64_t Vc = (a.V - j0 < a.chunk) ? (a.V - j0) : a.chunk;
+  const char* sbase = a.logits + (row * a.ld + j0) * ESZ;
+  const int64_t y = a.labels[row];
+  const bool ignored = (y == a.ignore);
+  const bool badlab = !ignored && (y < 0 || y >= a.V);
+  if (ignored || badlab) {
+    if (tid == 0) a.slab_ms[bid] = make_double2(badlab ? __builtin_nan("") : -INFINITY, 0.0);
+    return;
+  }
+  const bool mine = y >= j0 && y < j0 + Vc;
+  const Geom g = geom<ESZ, EPV>(sbase, Vc);
+  const u32x4* body = (const u32x4*)(sbase + g.head * ESZ);
+  u32x4 v[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = k * NT + tid;
+    if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
+  }
+  const bool has_h = tid < g.head, has_t = tid < g.tail;
+  float xh = -INFINITY, xt = -INFINITY;
+  if (has_h) xh = T::load1(((const B*)sbase)[tid]);
+  if (has_t) xt = T::load1(((const B*)sbase)[g.head + (int64_t)g.nvec * EPV + tid]);
+  if (mine && tid == 0) a.slab_xy[row] = T::load1(((const B*)sbase)[y - j0]);
+  const Owner own = owner<NT, EPV>(g, mine ? y - j0 : -1, tid);
+  A m, s;
+  if constexpr (ESZ == 2) {
+    float mf = fmaxf(xh, xt), mn = INFINITY;
+    pass0_16<T, NT, VPL>(v, g.nvec, tid, mf, mn);
+    if (own.head > 0) xh = -INFINITY;
+    if (own.tail > 0) xt = -INFINITY;
+    if (own.k >= 0) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        if (k == own.k) T::kill(v[k], own.e);
+    }
+    const float mc = (mf == -INFINITY) ? 0.0f : mf * kLog2e;
+    s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh, xt);
+    m = mf;
+  } else {
+    float mf = fmaxf(xh, xt);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if (k * NT + tid < g.nvec)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mf = fmaxf(mf, as<float>(v[k][d]));
+    if (own.head > 0) xh = -INFINITY;
+    if (own.tail > 0) xt = -INFINITY;
+    if (own.k >= 0) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        if (k == own.k) T::kill(v[k], own.e);
+    }
+    const double mm = (mf == -INFINITY) ? 0.0 : (double)mf;
+    s = exp((double)xh - mm) + exp((double)xt - mm);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if (k * NT + tid < g.nvec)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s += exp((double)as<float>(v[k][d]) - mm);
+    m = mf;
+  }
+  wave_ms(m, s);
+  if (lane == 0) {
+    lds_m[wid] = m;
+    lds_s[wid] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    A M = lds_m[0], S = lds_s[0];
+    for (int w = 1; w < NW; ++w) ms_merge(M, S, lds_m[w], lds_s[w]);
+    a.slab_ms[bid] = make_double2((double)M, (double)S);
+  }
+}
+
+// Merge of the C slab partials of a row (fp64): lse, loss, pcomp.
+struct RowStats {
+  double lse, loss, pcomp;
+  bool bad;
+};
+__device__ __forceinline__ RowStats merge_slabs(const Args& a, int64_t row) {
+  RowStats r;
+  double M = -INFINITY, S_ex = 0.0;
+  r.bad = false;
+  for (int c = 0; c < a.C; ++c) {
+    const double2 p = a.slab_ms[row * a.C + c];
+    if (p.x != p.x) r.bad = true;
+    ms_merge(M, S_ex, p.x, p.y);
+  }
+  if (r.bad) {
+    r.lse = r.loss = r.pcomp = __builtin_nan("");
+    return r;
+  }
+  const double xy = (double)a.slab_xy[row];
+  const double ey = exp(xy - M);
+  const double S = S_ex + ey;
+  r.lse = M + log(S);
+  r.pcomp = S_ex / S;
+  r.loss = (r.pcomp >= 0.5) ? (r.lse - xy) : log1p(S_ex / ey);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Chunked forward, step 2: per-row merge, row outputs and the mean.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(NT) void slab_merge_kernel(Args a) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  __shared__ double lds_d[NT];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint32_t epoch = ld_agent(&a.ws->epoch);
+  poll_to_lds(a, epoch + 1u, lds_u);
+  if (tid == 0) {
+    const int64_t y = a.labels[row];
+    RowStats r = {0.0, 0.0, 0.0, false};
+    if (y != a.ignore) r = merge_slabs(a, row);
+    a.loss_rows[row] = (float)r.loss;
+    if (a.lse_rows) a.lse_rows[row] = r.lse;
+    if (a.pcomp_rows) a.pcomp_rows[row] = r.pcomp;
+    publish_loss(a, row, (float)r.loss, epoch + 1u);
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    __syncthreads();
+    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked fused path (16-bit formats), step 2: merge the row's slab partials,
+// re-read the slab and write its gradient in place; row outputs from slab 0;
+// the mean at the end.  blockIdx.x = row * C + c.
+// ---------------------------------------------------------------------------
+template <typename T, int NT, int VPL, int POL>
+__global__ __launch_bounds__(NT) void slab_grad_kernel(Args a) {
+  constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
+  typedef typename T::bits_t B;
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  __shared__ double lds_d[NT];
+  __shared__ double lds_r[4];
+  const int tid = threadIdx.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t row = bid / a.C;
+  const int c = (int)(bid % a.C);
+  const uint32_t epoch = ld_agent(&a.ws->epoch);
+  const int64_t j0 = (int64_t)c * a.chunk;
+  const int64_t Vc = (a.V - j0 < a.chunk) ? (a.V - j0) : a.chunk;
+  char* sbase = a.logits + (row * a.ld + j0) * ESZ;
+  const int64_t y = a.labels[row];
+  const bool ignored = (y == a.ignore);
+  const Geom g = geom<ESZ, EPV>(sbase, Vc);
+  u32x4* body = (u32x4*)(sbase + g.head * ESZ);
+  u32x4 v[VPL];
+  if (!ignored) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = k * NT + tid;
+      if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
+    }
+  }
+  poll_to_lds(a, epoch + 1u, lds_u);
+  if (tid == 0 && !ignored) {
+    const RowStats r = merge_slabs(a, row);
+    lds_r[0] = r.lse;
+    lds_r[1] = r.loss;
+    lds_r[2] = r.pcomp;
+    lds_r[3] = r.bad ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  if (ignored) {
+    zero_row<T, NT, VPL, POL>(sbase, g, tid, 0);
+  } else {
+    const bool badlab = lds_r[3] != 0.0;
+    if (badlab) {
+      nan_row<T, NT, VPL, POL>(sbase, g, tid, 0);
+    } else {
+      const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+      const float scale = (float)scale_d, lse = (float)lds_r[0];
+      const bool hh = tid < g.head, ht = tid < g.tail;
+      const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
+      const float xh = hh ? T::load1(((const B*)sbase)[tid]) : 0.0f;
+      const float xt = ht ? T::load1(((const B*)sbase)[jt]) : 0.0f;
+      float tmin = INFINITY;
+      if constexpr (T::kBF) {
+        float mn = lane_min_16<T, NT, VPL>(v, g.nvec, tid, INFINITY);
+        if (hh) mn = fminf(mn, xh);
+        if (ht) mn = fminf(mn, xt);
+        tmin = (mn - fabsf(mn) * 0x1p-7f - lse) * kLog2e;
+      }
+      const int mode = block_grad_mode<T>(scale, tmin);
+      const GradConsts kc = grad_consts<T>(lse, scale, scale_d, lds_r[2]);
+      const Owner own = owner<NT, EPV>(g, (y >= j0 && y < j0 + Vc) ? y - j0 : -1, tid);
+      grad_row_16<T, NT, VPL, POL>(v, g.nvec, tid, body, mode, kc, own, xh, xt, hh ? (B*)sbase + tid : nullptr,
+                                   ht ? (B*)sbase + jt : nullptr);
+    }
+  }
+  if (c == 0 && tid == 0) {
+    const float loss = ignored ? 0.0f : (float)lds_r[1];
+    a.loss_rows[row] = loss;
+    if (a.lse_rows) a.lse_rows[row] = ignored ? 0.0 : lds_r[0];
+    if (a.pcomp_rows) a.pcomp_rows[row] = ignored ? 0.0 : lds_r[2];
+    publish_loss(a, row, loss, epoch + 1u);
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    __syncthreads();
+    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+  }
+}
+
+// Writes the outputs of a call with no rows (L = NaN, n_valid = 0).
+__global__ void empty_call_kernel(float* loss_mean, int32_t* n_valid, uint32_t* status) {
+  if (threadIdx.x == 0) {
+    loss_mean[0] = __builtin_nanf("");
+    n_valid[0] = 0;
+    if (status) status[0] = 0u;
+  }
+}
+
+// Zero-fills a workspace with plain stores.
+__global__ void ws_fill_kernel(uint32_t* p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace cek

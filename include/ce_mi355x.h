@@ -1,0 +1,160 @@
+/*
+ * ce_mi355x.h -- C ABI of the MI355X (gfx950) token-level softmax
+ * cross-entropy library: forward, backward, and the fused forward+backward
+ * that writes the gradient over the logits.
+ *
+ * The operation.  The pages name a "Fast Cross Entropy" kernel (PyPI page
+ * "fms-acceleration-foak 0.7.4", kernel list) that replaces a causal LM's
+ * cross-entropy loss (fms-acceleration PR #79, "Bug Fix to Model Patcher":
+ * FastCrossEntropyLoss is patched in for the model's loss) and is used for full
+ * fine-tuning, LoRA and padding-free packed batches (fms-hf-tuning PR #280,
+ * "Notes on FastKernels").  It computes, for each logit row x[0..V) with label
+ * y, the textbook softmax cross-entropy:
+ *
+ *   lse   = log sum_j exp(x_j)                      (stable: max subtracted)
+ *   loss  = lse - x_y                               (nats)
+ *   L     = sum over valid rows of loss / n_valid   (token mean: PR #280,
+ *                                                    "Early Version Of This
+ *                                                    Plugin", per-token averaging)
+ *   grad_j = (dloss / n_valid) * (exp(x_j - lse) - [j == y])
+ *
+ * A row whose label equals ignore_index is not valid: its loss is 0, its
+ * gradient row is +0, and it is not counted in n_valid.  The default
+ * ignore_index of the callers is -100.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a device pointer owned by the caller; the
+ *     library allocates no memory and keeps no pointer after return.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream).  No entry point synchronises the stream or reads device data on
+ *     the host; outputs are valid once the stream work completes, and inputs
+ *     must stay alive until then.
+ *   - logits: n_rows rows of `vocab` elements of `dtype`, row i starting at
+ *     element i * ld (ld >= vocab).  The pointer must be aligned to the element
+ *     size; any 16-byte misalignment is handled.
+ *   - labels: n_rows int64 class indices.
+ *   - Host-checkable errors return a nonzero code before anything is enqueued.
+ *     A HIP launch failure returns CE_ERR_HIP.
+ *   - Errors only the device can see are OR-ed into the status word (see
+ *     CE_STATUS_*): a label outside [0, vocab) that is not ignore_index makes
+ *     that row's loss and gradient NaN, still counts the row in n_valid, and
+ *     sets CE_STATUS_LABEL_RANGE.
+ *   - Calls that share a workspace must be ordered (same stream, or joined by
+ *     events); calls with different workspaces are independent.
+ *   - Results are deterministic: the same inputs give the same bits.
+ *   - Precision: bf16/fp16 inputs are computed in fp32 and the gradient is
+ *     rounded once to the input format (nearest-even, subnormals kept); fp32
+ *     inputs are computed in fp64 and rounded once to fp32.
+ */
+#ifndef CE_MI355X_H
+#define CE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CE_ABI_VERSION 1
+
+/* element formats of logits and gradients */
+enum ce_dtype { CE_DTYPE_F32 = 0, CE_DTYPE_BF16 = 1, CE_DTYPE_F16 = 2 };
+
+/* return codes */
+enum ce_error {
+  CE_OK = 0,
+  CE_ERR_INVALID_ARG = 1, /* bad size, stride, pointer or alignment */
+  CE_ERR_DTYPE = 2,       /* unknown dtype */
+  CE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than ce_workspace_bytes() */
+  CE_ERR_UNSUPPORTED = 4, /* a valid request this build does not serve */
+  CE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+};
+
+/* bits OR-ed into the status word by the kernels */
+#define CE_STATUS_LABEL_RANGE 0x1u  /* some label outside [0, vocab) and not ignore_index */
+#define CE_STATUS_SYNC_TIMEOUT 0x2u /* a bounded inter-workgroup wait gave up: outputs invalid */
+
+/* ABI version of the loaded library (CE_ABI_VERSION it was built with). */
+int ce_abi_version(void);
+
+/* Static text for a return code or status bit. */
+const char* ce_error_string(int code);
+
+/*
+ * Bytes of device workspace the calls below need for this shape (0 < result;
+ * the same value serves ce_forward and ce_fwd_bwd_inplace).  chunk as below.
+ * Returns 0 for arguments that every entry point would reject.
+ */
+size_t ce_workspace_bytes(int64_t n_rows, int64_t vocab, int64_t chunk, int dtype);
+
+/*
+ * Prepare a workspace for first use (zero-fills it on `stream`).  Must be
+ * called once after allocating a workspace; every successful call leaves the
+ * workspace ready for the next one.  Also recovers a workspace after a call
+ * that reported CE_STATUS_SYNC_TIMEOUT.
+ */
+int ce_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward pass.
+ *   chunk         vocabulary slab width for the per-chunk log-sum-exp merge
+ *                 (lse = M + log sum_c exp(lse_c - M), M = max_c lse_c; PR #79
+ *                 "TODO": chunked loss).  0 = no chunking (the whole row is
+ *                 reduced at once when it fits on chip; larger rows are chunked
+ *                 at 65536 automatically).  The result does not depend on chunk
+ *                 beyond rounding.
+ *   loss_mean     out, 1 float: L (NaN when n_valid == 0).
+ *   loss_rows     out, n_rows floats: per-row loss (0 for ignored rows).
+ *   lse_rows      out or NULL, n_rows doubles: per-row lse (0 for ignored rows).
+ *   pcomp_rows    out or NULL, n_rows doubles: 1 - softmax(x)_y, the complement
+ *                 of the label's probability, computed without cancellation
+ *                 (0 for ignored rows).  ce_backward needs lse and pcomp; they
+ *                 are kept in fp64 so that a backward of fp32 logits can round
+ *                 its gradient as tightly as the fused call does.
+ *   n_valid       out, 1 int32.
+ *   status        out or NULL, 1 uint32: CE_STATUS_* bits of this call.
+ * logits is not modified.
+ */
+int ce_forward(const void* logits, int64_t ld, const int64_t* labels, int64_t n_rows,
+               int64_t vocab, int dtype, int64_t ignore_index, int64_t chunk,
+               float* loss_mean, float* loss_rows, double* lse_rows, double* pcomp_rows,
+               int32_t* n_valid, uint32_t* status, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * Backward pass from the forward's saved per-row lse and pcomp:
+ *   grad_j = s * exp(x_j - lse)  (j != y),   grad_y = -s * pcomp,
+ *   s = dloss / n_valid;  ignored rows get +0.
+ *   dloss     device float or NULL (= 1.0): the upstream gradient of L.
+ *   n_valid   device int32 from the forward.
+ *   grad      n_rows rows of `vocab` elements of dtype, row i at i * grad_ld.
+ *             May be the logits buffer itself (in place, grad_ld == ld); if it
+ *             is a different buffer it must not overlap logits and must share
+ *             the logits' 16-byte alignment (grad % 16 == logits % 16 and
+ *             grad_ld * esize % 16 == ld * esize % 16), else
+ *             CE_ERR_UNSUPPORTED.
+ */
+int ce_backward(const void* logits, int64_t ld, const int64_t* labels, const double* lse_rows,
+                const double* pcomp_rows, const int32_t* n_valid, const float* dloss,
+                int64_t n_rows, int64_t vocab, int dtype, int64_t ignore_index, void* grad,
+                int64_t grad_ld, void* stream);
+
+/*
+ * Fused forward + backward: the outputs of ce_forward, and the gradient of
+ * dloss * L written over the logits.  With no chunking and rows that fit on
+ * chip (vocab <= 131072 for bf16/fp16, <= 65536 for fp32) this is one kernel
+ * that reads every valid row once and writes every row once; ignored rows are
+ * written without being read.  dloss: device float or NULL (= 1.0).
+ */
+int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t n_rows,
+                       int64_t vocab, int dtype, int64_t ignore_index, int64_t chunk,
+                       const float* dloss, float* loss_mean, float* loss_rows, double* lse_rows,
+                       double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CE_MI355X_H */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/ce_mi355x.h declares, and rejects bad arguments before it
+enqueues anything.  Every call below must fail validation -- none may reach a
+kernel launch, because the pointers are fake."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_entropy_loss_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce_mi355x.h")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+VP = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ce_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.ce_abi_version() == _lib.ABI_VERSION
+    for code in range(6):
+        assert len(lib.ce_error_string(code)) > 0
+    assert b"unknown" in lib.ce_error_string(99)
+
+
+def test_workspace_bytes(lib):
+    whole = lib.ce_workspace_bytes(4096, 32000, 0, _lib.CE_DTYPE_BF16)
+    chunked = lib.ce_workspace_bytes(8192, 128256, 65536, _lib.CE_DTYPE_BF16)
+    assert 0 < whole <= 1024 + 4096 * 8 + 256  # header + one tagged loss slot per row
+    assert chunked >= 8192 * 2 * 16 + 8192 * 4
+    auto = lib.ce_workspace_bytes(8, 300000, 0, _lib.CE_DTYPE_BF16)  # > on-chip row: auto-chunked
+    assert auto > lib.ce_workspace_bytes(8, 30000, 0, _lib.CE_DTYPE_BF16)
+    assert lib.ce_workspace_bytes(-1, 10, 0, 1) == 0
+    assert lib.ce_workspace_bytes(4, 0, 0, 1) == 0
+    assert lib.ce_workspace_bytes(4, 10, -1, 1) == 0
+    assert lib.ce_workspace_bytes(4, 10, 0, 7) == 0
+    assert lib.ce_workspace_bytes(4, 300000, 200000, 1) == 0  # chunk wider than a workgroup holds
+
+
+def fused(lib, logits=FAKE, ld=100, labels=FAKE, N=4, V=100, dtype=1, ignore=-100, chunk=0, dloss=None,
+          loss_mean=FAKE, loss_rows=FAKE, lse=FAKE, pcomp=FAKE, n_valid=FAKE, status=FAKE, ws=FAKE,
+          ws_bytes=1 << 20):
+    return lib.ce_fwd_bwd_inplace(VP(logits), ld, VP(labels), N, V, dtype, ignore, chunk, VP(dloss),
+                                  VP(loss_mean), VP(loss_rows), VP(lse), VP(pcomp), VP(n_valid), VP(status),
+                                  VP(ws), ws_bytes, None)
+
+
+def forward(lib, **kw):
+    d = dict(logits=FAKE, ld=100, labels=FAKE, N=4, V=100, dtype=1, ignore=-100, chunk=0, loss_mean=FAKE,
+             loss_rows=FAKE, lse=FAKE, pcomp=FAKE, n_valid=FAKE, status=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    d.update(kw)
+    return lib.ce_forward(VP(d["logits"]), d["ld"], VP(d["labels"]), d["N"], d["V"], d["dtype"], d["ignore"],
+                          d["chunk"], VP(d["loss_mean"]), VP(d["loss_rows"]), VP(d["lse"]), VP(d["pcomp"]),
+                          VP(d["n_valid"]), VP(d["status"]), VP(d["ws"]), d["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.CE_ERR_DTYPE),
+    (dict(dtype=-1), _lib.CE_ERR_DTYPE),
+    (dict(N=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(N=1 << 31), _lib.CE_ERR_INVALID_ARG),
+    (dict(V=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(ld=99), _lib.CE_ERR_INVALID_ARG),
+    (dict(logits=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(labels=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(logits=FAKE + 1), _lib.CE_ERR_INVALID_ARG),      # not aligned to a bf16 element
+    (dict(logits=FAKE + 2, dtype=0), _lib.CE_ERR_INVALID_ARG),  # not aligned to an fp32 element
+    (dict(labels=FAKE + 4), _lib.CE_ERR_INVALID_ARG),
+    (dict(chunk=-5), _lib.CE_ERR_INVALID_ARG),
+    (dict(loss_mean=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(loss_rows=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(n_valid=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(ws=0), _lib.CE_ERR_WORKSPACE),
+    (dict(ws_bytes=100), _lib.CE_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.CE_ERR_WORKSPACE),            # workspace must be 256-byte aligned
+    (dict(V=300000, ld=300000, chunk=200000), _lib.CE_ERR_UNSUPPORTED),
+    (dict(N=8192, V=128256, ld=128256, chunk=65536, ws_bytes=4096), _lib.CE_ERR_WORKSPACE),
+])
+def test_fused_rejects(lib, kw, code):
+    assert fused(lib, **kw) == code
+    assert forward(lib, **kw) == code
+
+
+def backward(lib, logits=FAKE, ld=100, labels=FAKE, lse=FAKE, pcomp=FAKE, n_valid=FAKE, dloss=None, N=4, V=100,
+             dtype=1, ignore=-100, grad=FAKE, grad_ld=100):
+    return lib.ce_backward(VP(logits), ld, VP(labels), VP(lse), VP(pcomp), VP(n_valid), VP(dloss), N, V, dtype,
+                           ignore, VP(grad), grad_ld, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), _lib.CE_ERR_DTYPE),
+    (dict(lse=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(pcomp=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(n_valid=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(grad=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(grad_ld=99), _lib.CE_ERR_INVALID_ARG),
+    (dict(grad_ld=104), _lib.CE_ERR_INVALID_ARG),            # in place needs the same stride
+    (dict(grad=FAKE + 64), _lib.CE_ERR_INVALID_ARG),         # partial overlap with the logits
+    (dict(grad=FAKE + 4096 + 2), _lib.CE_ERR_UNSUPPORTED),   # different 16-byte phase
+    (dict(grad=FAKE + 4096, grad_ld=101), _lib.CE_ERR_UNSUPPORTED),
+    (dict(grad=FAKE + 4097), _lib.CE_ERR_INVALID_ARG),       # not element aligned
+])
+def test_backward_rejects(lib, kw, code):
+    assert backward(lib, **kw) == code
+
+
+def test_workspace_init_rejects(lib):
+    assert lib.ce_workspace_init(None, 4096, None) == _lib.CE_ERR_WORKSPACE
+    assert lib.ce_workspace_init(VP(FAKE), 100, None) == _lib.CE_ERR_WORKSPACE
+    assert lib.ce_workspace_init(VP(FAKE + 8), 4096, None) == _lib.CE_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "missing.so"))

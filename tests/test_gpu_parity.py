@@ -1,0 +1,282 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element,
+on seeded inputs (tolerances in tests/parity.py).  Every call goes through the
+C ABI (the ctypes binding only marshals pointers)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import cross_entropy_loss_amd as ce
+import oracle
+import workloads as wl
+from parity import REL, assert_grad_close, assert_rel, to_device, to_host_bits, ulp_distance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this machine")
+    ce._lib.load()  # raises when the library is missing
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_fused(bits, labels, dtype, dloss=1.0, chunk=0, ld=None, offset=0, ignore=-100):
+    _say(f"[fused] dtype={dtype} shape={bits.shape} ld={ld} offset={offset} chunk={chunk} dloss={dloss}")
+    x = to_device(bits, dtype, ld, offset)
+    y = torch.from_numpy(np.ascontiguousarray(labels)).cuda()
+    dl = torch.tensor([dloss], dtype=torch.float32, device="cuda")
+    out = ce.ce_fwd_bwd_inplace(x, y, ignore, chunk, dl)
+    torch.cuda.synchronize()
+    return out, x
+
+
+def check_against_oracle(out, grad_t, bits, labels, dtype, dloss=1.0, ignore=-100, expect_status=0):
+    ref = oracle.cross_entropy(bits, labels, dtype, ignore_index=ignore, dloss=dloss, allow_bad=True, threads=8)
+    valid = labels != ignore
+    n = int(out["n_valid"].item())
+    assert n == ref["n_valid"]
+    assert int(out["status"].item()) == expect_status
+    L = float(out["loss_mean"].item())
+    if ref["n_valid"] == 0 or ref["bad"]:
+        assert math.isnan(L)
+    else:
+        assert_rel(L, ref["loss_mean"], dtype, "loss_mean")
+    good = valid & ~np.isnan(ref["loss_rows"])
+    loss_rows = out["loss_rows"].cpu().numpy()
+    lse_rows = out["lse_rows"].cpu().numpy()
+    pcomp = out["pcomp_rows"].cpu().numpy()
+    assert_rel(loss_rows[good], ref["loss_rows"][good], dtype, "loss_rows")
+    assert_rel(lse_rows[good], ref["lse"][good], dtype, "lse_rows")
+    pc_ref = -np.expm1(-ref["loss_rows"][good])  # 1 - p_y from the oracle's loss
+    assert_rel(pcomp[good], pc_ref, dtype, "pcomp_rows")
+    assert (loss_rows[~valid] == 0).all() and (lse_rows[~valid] == 0).all()
+    bad_rows = valid & np.isnan(ref["loss_rows"])
+    assert np.isnan(loss_rows[bad_rows]).all()
+    g = to_host_bits(grad_t, dtype)
+    if bad_rows.any():
+        gv = g[bad_rows].view(np.float32) if dtype == "f32" else g[bad_rows]
+        if dtype == "f32":
+            assert np.isnan(gv).all()
+        else:
+            assert ((gv & 0x7FFF) > (0x7F80 if dtype == "bf16" else 0x7C00)).all()
+    rows_ok = ~bad_rows
+    assert_grad_close(g[rows_ok], ref["grad"][rows_ok], dtype, "grad")
+    zero = g[~valid].view(np.uint32 if dtype == "f32" else np.uint16)
+    assert (zero == 0).all(), "ignored rows must be +0"
+    return ref
+
+
+# ---------------------------------------------------------------------------
+
+def test_config1_tiny():
+    w = wl.WORKLOADS[1]
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, w.dtype)
+    check_against_oracle(out, g, bits, p.labels, w.dtype)
+
+
+RAGGED = [(d, V) for d in ("bf16", "f16") for V in (1, 2, 3, 7, 8, 9, 17, 1000, 1023, 2049, 4097, 32001)] + \
+         [("f32", V) for V in (1, 3, 4, 5, 999, 4097, 16385)]
+
+
+@pytest.mark.parametrize("dtype,V", RAGGED, ids=[f"{d}-V{v}" for d, v in RAGGED])
+def test_ragged_rows(dtype, V):
+    w = wl.custom(f"ragged-{dtype}-{V}", 100 + V, 37, V, dtype, 30.0 if dtype == "f16" else 2.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+
+
+@pytest.mark.parametrize("V", [32000, 32005, 49152, 65536, 98304, 128256])
+def test_tiles_and_tails_bf16(V):
+    # the whole-row kernel at several capacities, with a ragged last vector
+    w = wl.custom(f"tiles-{V}", 7 + V, 24, V, "bf16", 3.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, "bf16")
+    check_against_oracle(out, g, bits, p.labels, "bf16")
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_config_rows(k):
+    # the first 96 rows of each workload at its real vocabulary, chunking and dloss
+    w = wl.WORKLOADS[k]
+    p = wl.plan(w)
+    rows = np.arange(96)
+    bits = wl.logits(w, rows, p)
+    labels = p.labels[rows]
+    out, g = run_fused(bits, labels, w.dtype, dloss=w.dloss, chunk=w.chunk)
+    check_against_oracle(out, g, bits, labels, w.dtype, dloss=w.dloss)
+
+
+@pytest.mark.parametrize("dtype,ld,offset", [("bf16", 1003, 1), ("bf16", 1000, 3), ("f16", 1007, 5),
+                                             ("f32", 1001, 1), ("f32", 1000, 2)])
+def test_strided_and_unaligned(dtype, ld, offset):
+    w = wl.custom(f"strided-{dtype}", 17, 29, 1000, dtype, 2.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype, ld=ld, offset=offset)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+
+
+CHUNKS = [("f32", 1000, c) for c in (1, 7, 128, 999, 1000)] + \
+         [("bf16", 4097, c) for c in (1, 1000, 4096)] + [("f16", 3000, 1024), ("bf16", 70000, 65536)]
+
+
+@pytest.mark.parametrize("dtype,V,chunk", CHUNKS, ids=[f"{d}-V{v}-c{c}" for d, v, c in CHUNKS])
+def test_chunked(dtype, V, chunk):
+    N = 64 if V <= 1000 else 12
+    w = wl.custom(f"chunk-{dtype}-{V}", 5, N, V, dtype, 1.0 if dtype == "f32" else 2.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype, chunk=chunk)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+
+
+def test_no_valid_rows():
+    bits = wl.to_storage(np.random.default_rng(1).normal(0, 2, (9, 500)), "bf16")
+    labels = np.full(9, -100, np.int64)
+    out, g = run_fused(bits, labels, "bf16")
+    assert int(out["n_valid"].item()) == 0 and math.isnan(float(out["loss_mean"].item()))
+    assert (to_host_bits(g, "bf16") == 0).all()
+
+
+@pytest.mark.parametrize("dloss", [0.0, -1.0, 0.5, 65536.0])
+def test_dloss_values(dloss):
+    w = wl.custom("dloss", 23, 40, 1000, "bf16", 2.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, "bf16", dloss=dloss)
+    check_against_oracle(out, g, bits, p.labels, "bf16", dloss=dloss)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_bad_label(dtype):
+    w = wl.custom("badlabel", 29, 16, 300, dtype, 2.0, 0.1)
+    bits, p = wl.make(w)
+    labels = p.labels.copy()
+    labels[3] = 300
+    labels[7] = -5
+    out, g = run_fused(bits, labels, dtype)
+    check_against_oracle(out, g, bits, labels, dtype, expect_status=ce.CE_STATUS_LABEL_RANGE)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_ignore_index_inside_range(dtype):
+    w = wl.custom("ign3", 31, 40, 50, dtype, 2.0, 0.0)
+    bits, p = wl.make(w)
+    labels = p.labels.copy()
+    labels[::4] = 3
+    out, g = run_fused(bits, labels, dtype, ignore=3)
+    check_against_oracle(out, g, bits, labels, dtype, ignore=3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_confident_rows(dtype):
+    rng = np.random.default_rng(4)
+    V = 3000
+    x = rng.normal(0, 1, (12, V))
+    y = rng.integers(0, V, 12).astype(np.int64)
+    for i, A in enumerate((6.0, 12.0, 20.0, 30.0, 40.0, 60.0)):
+        x[i, y[i]] = A                     # label dominates: p_y -> 1
+        x[i + 6, (y[i + 6] + 1) % V] = A   # another column dominates: p_y -> 0
+    bits = wl.to_storage(x, dtype)
+    out, g = run_fused(bits, y, dtype)
+    check_against_oracle(out, g, bits, y, dtype)
+
+
+@pytest.mark.parametrize("dtype,sigma,n", [("bf16", 40.0, 5), ("bf16", 60.0, 3), ("f16", 30.0, 16),
+                                           ("f32", 40.0, 5)])
+def test_wide_rows_subnormal_outputs(dtype, sigma, n):
+    # few rows (large dloss / n) and wide logit spread: outputs reach the
+    # format's subnormal range, where a flushed exponential would show
+    w = wl.custom("wide", 41, n, 2000, dtype, sigma, 0.0)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype, dloss=1.0)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+
+
+def test_deterministic():
+    w = wl.custom("det", 43, 300, 32000, "bf16", 2.0, 0.05)
+    bits, p = wl.make(w)
+    a, ga = run_fused(bits, p.labels, "bf16")
+    b, gb = run_fused(bits, p.labels, "bf16")
+    assert (to_host_bits(ga, "bf16") == to_host_bits(gb, "bf16")).all()
+    for k in ("loss_mean", "loss_rows", "lse_rows", "pcomp_rows", "n_valid"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype,V,chunk", [("bf16", 32000, 0), ("f16", 5000, 0), ("f32", 1000, 0),
+                                           ("bf16", 70000, 32768), ("f32", 3000, 1000)])
+def test_split_forward_backward(dtype, V, chunk):
+    w = wl.custom("split", 47, 20, V, dtype, 2.0, 0.1)
+    bits, p = wl.make(w)
+    _say(f"[split] dtype={dtype} V={V} chunk={chunk}")
+    x = to_device(bits, dtype)
+    y = torch.from_numpy(p.labels).cuda()
+    dl = torch.tensor([0.75], dtype=torch.float32, device="cuda")
+    f = ce.ce_forward(x, y, chunk=chunk)
+    grad = ce.ce_backward(x, y, f["lse_rows"], f["pcomp_rows"], f["n_valid"], dl)
+    torch.cuda.synchronize()
+    assert (to_host_bits(x, dtype) == bits).all(), "ce_forward must not modify the logits"
+    check_against_oracle(f, grad, bits, p.labels, dtype, dloss=0.75)
+    # in place through the same entry point
+    ce.ce_backward(x, y, f["lse_rows"], f["pcomp_rows"], f["n_valid"], dl, grad=x)
+    torch.cuda.synchronize()
+    assert (to_host_bits(x, dtype) == to_host_bits(grad, dtype)).all()
+
+
+def test_autograd_module():
+    w = wl.custom("autograd", 53, 2 * 33, 1000, "bf16", 2.0, 0.1)
+    bits, p = wl.make(w)
+    _say("[autograd] bf16 66x1000")
+    x = to_device(bits, "bf16").clone().requires_grad_(True)
+    y = torch.from_numpy(p.labels).cuda()
+    loss_fn = ce.FastCrossEntropyLoss()
+    L = loss_fn(x.view(2, 33, 1000), y.view(2, 33))
+    (L * 3.0).backward()
+    ref = oracle.cross_entropy(bits, p.labels, "bf16", dloss=3.0)
+    assert abs(float(L) - ref["loss_mean"]) <= REL["bf16"] * ref["loss_mean"]
+    assert_grad_close(to_host_bits(x.grad, "bf16"), ref["grad"], "bf16", "autograd grad")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times:
+# the mean and n_valid against the oracle over every row, the gradient of a
+# sample of rows element by element, and properties of every row.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_full_size(k):
+    w = wl.WORKLOADS[k]
+    p = wl.plan(w)
+    _say(f"[full] generating workload {k} {w.name} N={w.N} V={w.V}")
+    bits = wl.logits(w, None, p, threads=16)
+    out, g = run_fused(bits, p.labels, w.dtype, dloss=w.dloss, chunk=w.chunk)
+    n_full = int((p.labels != -100).sum())
+    assert int(out["n_valid"].item()) == n_full and int(out["status"].item()) == 0
+    _say("[full] oracle forward over every row")
+    fwd = oracle.rows(bits, p.labels, w.dtype, w.dloss / n_full, want_grad=False, threads=16)
+    L_ref = oracle.mean(fwd["loss"], p.labels)
+    assert_rel(float(out["loss_mean"].item()), L_ref, w.dtype, "loss_mean")
+    valid = p.labels != -100
+    assert_rel(out["loss_rows"].cpu().numpy()[valid], fwd["loss"][valid], w.dtype, "loss_rows")
+    rng = np.random.default_rng(99)
+    sample = np.unique(np.concatenate([rng.choice(w.N, 40, replace=False), [0, w.N - 1],
+                                       p.spike_rows[:4], p.spike_rows[-4:]]).astype(np.int64))
+    ref = oracle.rows(bits[sample], p.labels[sample], w.dtype, w.dloss / n_full, threads=16)
+    got = to_host_bits(g[torch.from_numpy(sample).cuda()], w.dtype)
+    assert_grad_close(got, ref["grad"], w.dtype, "sampled rows")
+    # every ignored row is +0; every valid row's gradient sums to ~0
+    gi = g[torch.from_numpy(~valid).cuda()]
+    assert int((gi.view(torch.int16) != 0).sum().item()) == 0
+    # each element is rounded once: relative 2^-9 (bf16) / 2^-12 (fp16) of
+    # sum |g| = 2 s (1 - p_y), plus half a subnormal ulp per element
+    half_sub = 2.0 ** -134 if w.dtype == "bf16" else 2.0 ** -25
+    s = w.dloss / n_full
+    rs = g[torch.from_numpy(valid).cuda()].float().sum(dim=1).abs().max().item()
+    assert rs <= 2 ** -7 * s + w.V * half_sub + 1e-9 * s
