@@ -14,6 +14,15 @@ The call is one kernel (rows fit on chip), so the same events time the
 dominant kernel for the roofline figure.
 
     python bench.py [--steps K] [--warmup W] [--workload 2]
+
+Profiling (rocprofv3 databases -> profiles/ summaries):
+    rocprofv3 --kernel-trace --stats -d D -o trace -- python bench.py --steps 10 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- python bench.py --steps 5 --no-cpu-baseline --calibrate
+    rocprofv3 --pmc WRITE_SIZE -d D -o write -- python bench.py --steps 5 --no-cpu-baseline --calibrate
+    python bench.py --profile-summary D
+--calibrate also runs a plain copy of the logits' size with the kernels'
+16-byte nontemporal loads and stores: the counters' reading of that copy
+gives the factor that turns FETCH_SIZE / WRITE_SIZE into bytes.
 """
 from __future__ import annotations
 
@@ -64,21 +73,107 @@ def measured_traffic(name: str):
     return c.get("traffic_bytes")
 
 
-def cpu_baseline(w, bits, labels, max_seconds=20.0):
+def cpu_baseline(w, bits, labels, max_seconds=20.0, min_seconds=5.0):
+    """The float64 oracle (forward + backward of every sampled row) on the host
+    cores: a bounded sample of the workload's rows, repeated until at least
+    min_seconds of work so the rate is stable."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
     n = int((labels != -100).sum())
-    # a bounded sample of rows, sized from a small calibration run
     t0 = time.perf_counter()
     oracle.rows(bits[:64], labels[:64], w.dtype, w.dloss / n, threads=threads)
     per_row = (time.perf_counter() - t0) / 64
     rows = int(min(w.N, max(64, max_seconds / 2 / max(per_row, 1e-9))))
-    t0 = time.perf_counter()
-    oracle.rows(bits[:rows], labels[:rows], w.dtype, w.dloss / n, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {w.N} rows of {w.name}: float64 forward + backward, "
-                      f"{threads} threads, {dt:.2f} s"}
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.rows(bits[:rows], labels[:rows], w.dtype, w.dloss / n, threads=threads)
+        done += rows
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt >= max_seconds:
+            break
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.N} rows of {w.name}, {done // rows} passes: float64 forward + "
+                      f"backward, {threads} threads, {dt:.2f} s"}
+
+
+def _db_rows(path, sql):
+    import sqlite3
+    con = sqlite3.connect(path)
+    try:
+        return con.execute(sql).fetchall()
+    finally:
+        con.close()
+
+
+def profile_summary(d: str, workload: int) -> None:
+    """Reads rocprofv3 databases (trace_results.db, fetch_results.db,
+    write_results.db under d) and writes profiles/<kernel>_<workload>.txt and
+    the counters JSON that bench.py reads for roofline.traffic."""
+    import glob
+    import workloads as wl
+    w = wl.WORKLOADS[workload]
+    labels = wl.plan(w).labels
+    find = lambda stem: (glob.glob(os.path.join(d, "**", f"{stem}_results.db"), recursive=True) or [None])[0]
+    trace, fetch, write = find("trace"), find("fetch"), find("write")
+    lines = [f"# rocprofv3 summary: fused cross-entropy forward+backward, workload {w.name}",
+             f"# N={w.N} V={w.V} dtype={w.dtype} chunk={w.chunk}; kernel sources sha {kernel_sha()}",
+             "# commands (from the repository root):",
+             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- python bench.py --steps 10 --no-cpu-baseline",
+             "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- python bench.py --steps 5 --no-cpu-baseline --calibrate",
+             "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- python bench.py --steps 5 --no-cpu-baseline --calibrate",
+             f"#   python bench.py --profile-summary D --workload {workload}", ""]
+    ce_names = ("row_kernel", "row_fused", "slab_", "grad_kernel")
+    dominant = None
+    if trace:
+        rows = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
+                               "group by name order by sum(duration) desc")
+        lines.append("kernel-trace (durations in us; the first calls of a run are cold):")
+        lines.append(f"  {'kernel':70s} {'calls':>5s} {'avg':>9s} {'median':>9s} {'min':>9s} {'max':>9s}")
+        for name, n, avg, mn, mx in rows:
+            durs = sorted(r[0] for r in _db_rows(trace, "select duration from kernels where name = '%s'"
+                                                       % name.replace("'", "''")))
+            med = durs[len(durs) // 2]
+            lines.append(f"  {name[:70]:70s} {n:5d} {avg / 1e3:9.2f} {med / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}")
+            if dominant is None and any(c in name for c in ce_names):
+                dominant = (name, med / 1e3)
+        lines.append("")
+    abytes = algorithmic_bytes(w, labels)
+    logits_bytes = w.N * w.V * w.elem_bytes
+    rec = {"kernel_sha": kernel_sha(), "workload": w.name, "algorithmic_bytes": abytes}
+    for tag, db, counter in (("read", fetch, "FETCH_SIZE"), ("write", write, "WRITE_SIZE")):
+        if not db:
+            continue
+        rows = _db_rows(db, f"select kernel_name, avg(value), count(*) from counters_collection "
+                            f"where counter_name = '{counter}' group by kernel_name")
+        calib = [r for r in rows if "calib_copy" in r[0]]
+        ce = [r for r in rows if any(c in r[0] for c in ce_names)]
+        lines.append(f"{counter} (KiB per dispatch, as reported):")
+        for name, val, n in rows:
+            lines.append(f"  {name[:70]:70s} {val:14.1f}  ({n} dispatches)")
+        if calib and ce:
+            factor = (logits_bytes / 1024.0) / calib[0][1]
+            kib = sum(r[1] for r in ce)
+            rec[f"{tag}_kib_raw"] = kib
+            rec[f"{tag}_factor"] = factor
+            rec[f"{tag}_bytes"] = kib * 1024.0 * factor
+            lines.append(f"  calibration: copy of {logits_bytes} B reads as {calib[0][1]:.1f} KiB -> factor {factor:.4f}")
+            lines.append(f"  cross-entropy kernels: {kib:.1f} KiB x {factor:.4f} = {kib * 1024 * factor / 1e6:.2f} MB")
+        lines.append("")
+    if "read_bytes" in rec and "write_bytes" in rec:
+        rec["traffic_bytes"] = rec["read_bytes"] + rec["write_bytes"]
+        lines.append(f"HBM traffic per call: {rec['traffic_bytes'] / 1e6:.2f} MB "
+                     f"(algorithmic minimum {abytes / 1e6:.2f} MB, ratio {rec['traffic_bytes'] / abytes:.3f})")
+    if dominant:
+        rec["dominant_kernel"], rec["avg_us"] = dominant
+        lines.append(f"dominant kernel: {dominant[0]}  median {dominant[1]:.2f} us  "
+                     f"-> {abytes / (dominant[1] * 1e-6) / 1e9:.0f} GB/s algorithmic "
+                     f"({abytes / (dominant[1] * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f} GB/s)")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"ce_fused_{w.name}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", f"ce_fused_{w.name}.counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
 
 
 def main():
@@ -88,7 +183,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--profile-summary", metavar="DIR")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -134,6 +234,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if args.calibrate:
+        import ctypes
+        calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
+        calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        nbytes = pristine.numel() * pristine.element_size()
+        for _ in range(3):
+            flush.fill_(0)
+            rc = calib.ce_calib_copy(ctypes.c_void_p(pristine.data_ptr()), ctypes.c_void_p(work.data_ptr()), nbytes,
+                                     ctypes.c_void_p(stream.cuda_stream))
+            if rc:
+                raise SystemExit(f"calibration copy failed: {rc}")
+        torch.cuda.synchronize()
     st = int(out["status"].item())
     if st != 0:
         raise SystemExit(f"kernel status {st:#x}")

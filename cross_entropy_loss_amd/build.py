@@ -13,6 +13,8 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ce_api.hip")
 DEPS = [SRC, os.path.join(HERE, "csrc", "ce_kernels.h"), os.path.join(ROOT, "include", "ce_mi355x.h")]
 LIB = os.path.join(HERE, "libce_mi355x.so")
+CALIB_SRC = os.path.join(HERE, "csrc", "calib_copy.hip")
+CALIB_LIB = os.path.join(HERE, "libce_calib.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,18 +37,23 @@ def up_to_date() -> bool:
     return all(os.path.getmtime(d) <= t for d in DEPS)
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    """Compile the library (always when force=True)."""
-    if not force and up_to_date():
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp, SRC]
+def _compile(src: str, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile the library and the counter-calibration copy (always when force=True)."""
+    if not force and up_to_date() and os.path.exists(CALIB_LIB):
+        return LIB
+    _compile(SRC, LIB, verbose)
+    _compile(CALIB_SRC, CALIB_LIB, verbose)
     return LIB
 
 

@@ -14,7 +14,7 @@ using cek::Args;
 typedef void (*KernelFn)(Args);
 
 #ifndef CE_POL
-#define CE_POL 1  // nontemporal loads, write-back stores
+#define CE_POL 3  // nontemporal loads and stores (measured fastest for the fused rows)
 #endif
 constexpr int kPol = CE_POL;
 constexpr int64_t kMaxRows = 0x7fffffff;
@@ -89,6 +89,35 @@ int counters_for(int64_t N, int64_t G) {
   return (int)k;
 }
 
+// Co-resident workgroups of a kernel on the current device (cached per kernel).
+int64_t resident_blocks(KernelFn fn, int block) {
+  static KernelFn fns[64];
+  static int64_t vals[64];
+  static int n = 0;
+  for (int i = 0; i < n; ++i)
+    if (fns[i] == fn) return vals[i];
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, block, 0) != hipSuccess) return 0;
+  const int64_t r = (int64_t)cus * per_cu;
+  if (n < 64) {
+    fns[n] = fn;
+    vals[n] = r;
+    ++n;
+  }
+  return r;
+}
+
+// Persistent grid for N rows: no more workgroups than are co-resident, and
+// the same number of rows for every workgroup where N allows it.
+int64_t persistent_grid(KernelFn fn, int block, int64_t N) {
+  int64_t cap = resident_blocks(fn, block);
+  if (cap <= 0 || cap > N) return N;
+  const int64_t per = (N + cap - 1) / cap;
+  return (N + per - 1) / per;
+}
+
 int launch(KernelFn fn, int64_t grid, int block, Args a, hipStream_t st) {
   if (grid <= 0) return CE_OK;
   if (grid > 0x7fffffff) return CE_ERR_UNSUPPORTED;
@@ -105,9 +134,12 @@ struct Cfg {
 const Cfg kCfgs[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 12}, {256, 16},
                      {512, 12}, {512, 16}, {1024, 12}, {1024, 16}};
 
+#ifndef CE_MIN_NT
+#define CE_MIN_NT 256  // smallest workgroup the row kernels use
+#endif
 Cfg pick_cfg(int64_t nvec_max) {
   for (const Cfg& c : kCfgs)
-    if ((int64_t)c.nt * c.vpl >= nvec_max) return c;
+    if (c.nt >= CE_MIN_NT && (int64_t)c.nt * c.vpl >= nvec_max) return c;
   return kCfgs[sizeof(kCfgs) / sizeof(kCfgs[0]) - 1];
 }
 
@@ -119,6 +151,14 @@ template <typename T, bool FUSED>
 KernelFn row16_fn(Cfg c) {
 #define MAKE(NT, VPL) \
   if (c.nt == NT && c.vpl == VPL) return cek::row_kernel_16<T, NT, VPL, kPol, FUSED>;
+  CE_CFG_CASES(MAKE)
+#undef MAKE
+  return nullptr;
+}
+template <typename T>
+KernelFn aligned_fn(Cfg c) {
+#define MAKE(NT, VPL) \
+  if (c.nt == NT && c.vpl == VPL) return cek::row_fused_aligned<T, NT, VPL, kPol>;
   CE_CFG_CASES(MAKE)
 #undef MAKE
   return nullptr;
@@ -217,8 +257,17 @@ int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int
   const int e = epv(dtype);
   if (sp.C == 1) {
     const Cfg c = pick_cfg((V + e - 1) / e);
-    a.K = counters_for(N, N);
-    return launch(row_fn(dtype, fused, c), N, c.nt, a, st);
+    KernelFn fn = row_fn(dtype, fused, c);
+    int64_t G = N;  // one workgroup per row
+    // rows wider than 64K 16-bit elements, 16-byte aligned: the persistent
+    // buffer-addressed kernel (one 1024-lane workgroup per CU sweeps rows)
+    const bool aligned = ((uintptr_t)logits % 16 == 0) && ((ld * esize(dtype)) % 16 == 0) && (V % e == 0);
+    if (fused && aligned && dtype != CE_DTYPE_F32 && c.nt == 1024) {
+      fn = (dtype == CE_DTYPE_BF16) ? aligned_fn<cek::BF16>(c) : aligned_fn<cek::F16>(c);
+      G = persistent_grid(fn, c.nt, N);
+    }
+    a.K = counters_for(N, G);
+    return launch(fn, G, c.nt, a, st);
   }
   // chunked: per-slab statistics, then merge (+ gradient)
   char* wsb = (char*)ws;

@@ -391,8 +391,9 @@ __device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t 
     for (int j = 0; j < B; ++j) {
       const int64_t i = base + (int64_t)j * NT + tid;
       if (i < a.N) {
+        // once one wait has expired the call is already invalid: stop waiting
         for (int it = 0; (uint32_t)(w[j] >> 32) != tag; ++it) {
-          if (it >= kSpinLimit) {
+          if (to || it >= kSpinLimit) {
             to = 1;
             break;
           }
@@ -451,19 +452,32 @@ __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int ti
   }
 }
 
-// pass 1: sum of 2^{x log2 e - mc} over the lane's elements.
+// pass 1: sum of 2^{x log2 e - mc} over the lane's elements, leaving out
+// element ex of vector kx (the label, in the lane that holds it; kx = -1
+// elsewhere).  The exclusion zeroes that term; the staged data is untouched.
 template <typename T, int NT, int VPL>
-__device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int tid, float mc, float xh, float xt) {
+__device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int tid, float mc, float xh, float xt,
+                                         int kx = -1, int ex = 0) {
   float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xh, kLog2e, -mc));
   float s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -mc));
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     if (k * NT + tid < nvec) {
+      float t[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t u = v[k][d];
-        s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(T::lo(u), kLog2e, -mc));
-        s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(T::hi(u), kLog2e, -mc));
+        t[2 * d] = __builtin_amdgcn_exp2f(__builtin_fmaf(T::lo(u), kLog2e, -mc));
+        t[2 * d + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(T::hi(u), kLog2e, -mc));
+      }
+      if (k == kx) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (e == ex) ? 0.0f : t[e];
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        s0 += t[2 * d];
+        s1 += t[2 * d + 1];
       }
     }
   }
@@ -491,11 +505,18 @@ __device__ __forceinline__ float gelem(float x, const GradConsts& k) {
   else return (float)(exp((double)x - k.lse_d) * k.scale_d);
 }
 
+// Next-row prefetch issued from pass 2: once vector k of the current row has
+// been consumed, the same registers receive vector k of the next row.
+struct Prefetch {
+  const u32x4* body;  // next row's aligned body (NULL: nothing to fetch)
+  int nvec;
+};
+
 // pass 2: gradient of the staged vectors, stored to gbody.  The label element
 // (held by lane/vector `own`) gets k.gy.
 template <typename T, int NT, int VPL, int POL, int MODE>
-__device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
-                                         const Owner& own) {
+__device__ __forceinline__ void pass2_16(u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
+                                         const Owner& own, const Prefetch& pf) {
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     const int idx = k * NT + tid;
@@ -515,6 +536,20 @@ __device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int ti
       for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
       stv<POL>(gbody + idx, o);
     }
+    // keep the prefetch after this vector's arithmetic: hoisting it would
+    // hold the old and the new row in registers at once
+    __builtin_amdgcn_sched_barrier(0);
+    if (pf.body && idx < pf.nvec) v[k] = ldv<POL>(pf.body + idx);
+  }
+}
+
+// Issues the loads of a row's body into v.
+template <int NT, int VPL, int POL>
+__device__ __forceinline__ void load_body(u32x4 (&v)[VPL], const Prefetch& pf, int tid) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int idx = k * NT + tid;
+    if (pf.body && idx < pf.nvec) v[k] = ldv<POL>(pf.body + idx);
   }
 }
 
@@ -551,6 +586,21 @@ __device__ __forceinline__ GradConsts grad_consts(float lse, float scale, double
   return k;
 }
 
+// Gradient of one row in fp64, read from memory (rows whose scale is not a
+// positive finite number, and bf16 rows whose outputs may be subnormal, where
+// v_exp_f32 would flush).  Out of line: it holds none of the caller's staged
+// registers.  Reads each element before writing it, lane by lane, so it may
+// run in place.
+template <typename T>
+__device__ __forceinline__ void grad_row_generic(const char* xrow, char* grow, int64_t V, int64_t y, double lse,
+                                              double scale, double gy, int tid, int nt) {
+  typedef typename T::bits_t B;
+  for (int64_t j = tid; j < V; j += nt) {
+    const double gd = (j == y) ? gy : exp((double)T::load1(((const B*)xrow)[j]) - lse) * scale;
+    ((B*)grow)[j] = T::store1((float)gd);
+  }
+}
+
 // Writes NaN over a row whose label is out of range.
 template <typename T, int NT, int VPL, int POL>
 __device__ __forceinline__ void nan_row(char* gbase, const Geom& g, int tid, int v0) {
@@ -573,20 +623,21 @@ __device__ __forceinline__ void nan_row(char* gbase, const Geom& g, int tid, int
 // to gbody, plus this lane's head element (to *ph) and tail element (to *pt)
 // when it has them.
 template <typename T, int NT, int VPL, int POL>
-__device__ __forceinline__ void grad_row_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, int mode,
+__device__ __forceinline__ void grad_row_16(u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, int mode,
                                             const GradConsts& kc, const Owner& own, float xh, float xt,
-                                            typename T::bits_t* ph, typename T::bits_t* pt) {
+                                            typename T::bits_t* ph, typename T::bits_t* pt,
+                                            const Prefetch& pf = Prefetch{nullptr, 0}) {
   float gh = 0.0f, gt = 0.0f;
   if (mode == kFold) {
-    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own, pf);
     gh = gscalar<T, kFold>(xh, own.head > 0, kc);
     gt = gscalar<T, kFold>(xt, own.tail > 0, kc);
   } else if (mode == kMul) {
-    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own, pf);
     gh = gscalar<T, kMul>(xh, own.head > 0, kc);
     gt = gscalar<T, kMul>(xt, own.tail > 0, kc);
   } else {
-    pass2_16<T, NT, VPL, POL, kF64>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kF64>(v, nvec, tid, gbody, kc, own, pf);
     gh = gscalar<T, kF64>(xh, own.head > 0, kc);
     gt = gscalar<T, kF64>(xt, own.tail > 0, kc);
   }
@@ -644,11 +695,16 @@ __device__ __forceinline__ void zero_row(char* gbase, const Geom& g, int tid, in
 // ---------------------------------------------------------------------------
 // Whole-row kernel for 16-bit formats (bf16, fp16).
 //   FUSED: forward + gradient written over the row.   !FUSED: forward only.
-// One workgroup of NT lanes per row; row capacity NT * VPL vectors.
+// One workgroup of NT lanes per row; row capacity NT * VPL vectors.  (A
+// persistent variant that loops over rows measured no faster at these row
+// sizes: the hardware refills a finished workgroup's slot within ~2 us.)
 // ---------------------------------------------------------------------------
+// At least 4 waves per SIMD: a 256-lane row workgroup stages 64 KB in 64
+// VGPRs and must leave room for four such rows per CU.
 template <typename T, int NT, int VPL, int POL, bool FUSED>
-__global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
+__global__ __launch_bounds__(NT, 4) void row_kernel_16(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
+  typedef typename T::bits_t B;
   __shared__ float lds_m[NW], lds_s[NW], lds_mn[NW];
   __shared__ uint32_t lds_u[2 * NW + 4];
   __shared__ double lds_d[NT];
@@ -664,19 +720,13 @@ __global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
   const bool ignored = (y == a.ignore);
   const bool badlab = !ignored && (y < 0 || y >= a.V);
   const Geom g = geom<ESZ, EPV>(rbase, a.V);
-  const u32x4* body = (const u32x4*)(rbase + g.head * ESZ);
-  typedef typename T::bits_t B;
 
   // ---- issue every load of the row -------------------------------------
   u32x4 v[VPL];
   float xh = -INFINITY, xt = -INFINITY;  // this lane's head / tail element
   const bool has_h = tid < g.head, has_t = tid < g.tail;
   if (!ignored) {
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const int idx = k * NT + tid;
-      if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
-    }
+    load_body<NT, VPL, POL>(v, Prefetch{(const u32x4*)(rbase + g.head * ESZ), g.nvec}, tid);
     if (has_h) xh = T::load1(((const B*)rbase)[tid]);
     if (has_t) xt = T::load1(((const B*)rbase)[g.head + (int64_t)g.nvec * EPV + tid]);
   }
@@ -691,15 +741,11 @@ __global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
     if (has_t) mn = fminf(mn, xt);
     pass0_16<T, NT, VPL>(v, g.nvec, tid, m, mn);
     const Owner own = owner<NT, EPV>(g, badlab ? -1 : y, tid);
-    if (own.head > 0) xh = -INFINITY;
-    if (own.tail > 0) xt = -INFINITY;
-    if (own.k >= 0) {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k)
-        if (k == own.k) T::kill(v[k], own.e);
-    }
+    // the label element is left out of the sum (its term is zeroed in the
+    // lane that holds it); the staged data itself is not modified
+    const float xh1 = (own.head > 0) ? -INFINITY : xh, xt1 = (own.tail > 0) ? -INFINITY : xt;
     const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-    float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh, xt);
+    float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh1, xt1, own.k, own.e);
     wave_ms(m, s);
     mn = wave_min(mn);
     if (lane == 0) {
@@ -734,10 +780,15 @@ __global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
         // lower bound of (x - lse) log2e over the row (bf16 lane minima are
         // lower bounds within one bf16 ulp; widen by 2^-7 relative)
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
-        typedef typename T::bits_t B;
-        grad_row_16<T, NT, VPL, POL>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), grad_mode<T>(scale, tmin), kc,
-                                     own, xh, xt, has_h ? (B*)gbase + tid : nullptr,
-                                     has_t ? (B*)gbase + g.head + (int64_t)g.nvec * EPV + tid : nullptr);
+        if (grad_mode<T>(scale, tmin) == kFold) {
+          pass2_16<T, NT, VPL, POL, kFold>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), kc, own,
+                                           Prefetch{nullptr, 0});
+          if (has_h) ((B*)gbase)[tid] = T::store1(gscalar<T, kFold>(xh, own.head > 0, kc));
+          if (has_t)
+            ((B*)gbase)[g.head + (int64_t)g.nvec * EPV + tid] = T::store1(gscalar<T, kFold>(xt, own.tail > 0, kc));
+        } else {
+          grad_row_generic<T>(rbase, gbase, a.V, y, (double)lse, scale_d, (double)kc.gy, tid, NT);
+        }
       }
     }
   } else {
@@ -750,6 +801,165 @@ __global__ __launch_bounds__(NT) void row_kernel_16(Args a) {
     publish_loss(a, row, loss, tag);
   }
   if (blockIdx.x == gridDim.x - 1) {
+    __syncthreads();
+    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused kernel for 16-byte-aligned 16-bit rows (vocab a multiple of 8 and a
+// 16-byte row stride), persistent, with buffer loads and stores.
+//
+// A buffer resource per row (SGPRs: base, byte size) lets every access use
+// one per-lane VGPR offset (lane * 16) plus a per-vector SGPR offset, so no
+// per-vector 64-bit addresses are held in VGPRs.  The descriptor's size also
+// bounds every access: loads past the row return 0 and stores past it are
+// dropped, so only the reductions of pass 0 / pass 1 need lane predicates.
+// The next row's loads are issued from pass 2 (see Prefetch above).
+// ---------------------------------------------------------------------------
+constexpr int kBufFlags = 0x00020000;  // raw 32-bit dword buffer, gfx9 layout
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kBufFlags);
+}
+// aux bits of buffer instructions on gfx94x/gfx950: sc0 = 1, nt = 2, sc1 = 16
+template <int POL>
+constexpr int aux_load() { return (POL & 1) ? 2 : 0; }
+template <int POL>
+constexpr int aux_store() { return (POL & 2) ? 2 : 0; }
+
+template <int NT, int VPL, int POL>
+__device__ __forceinline__ void buf_load_row(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k)
+    v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k * NT * 16, aux_load<POL>()));
+}
+template <int NT, int VPL, int POL>
+__device__ __forceinline__ void buf_fill_row(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t word) {
+  const u32x4 z = {word, word, word, word};
+#pragma unroll
+  for (int k = 0; k < VPL; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, z), rs, voff,
+                                           k * NT * 16, aux_store<POL>());
+}
+
+// pass 2 (folded scale) on buffer stores, with the next row's loads issued
+// into the registers each vector frees.  Lanes past the row compute garbage
+// that their dropped stores discard.
+template <typename T, int NT, int VPL, int POL, bool PF>
+__device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t out, __amdgpu_buffer_rsrc_t nxt,
+                                          uint32_t voff, const GradConsts& kc, int kx, int ex) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    float gv[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      gv[2 * d] = gelem<kFold>(T::lo(v[k][d]), kc);
+      gv[2 * d + 1] = gelem<kFold>(T::hi(v[k][d]), kc);
+    }
+    if (k == kx) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] = (e == ex) ? kc.gy : gv[e];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, o), out, voff,
+                                           k * NT * 16, aux_store<POL>());
+    if constexpr (PF) {
+      __builtin_amdgcn_sched_barrier(0);
+      v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nxt, voff, k * NT * 16, aux_load<POL>()));
+    }
+  }
+}
+
+template <typename T, int NT, int VPL, int POL>
+__global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
+  constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
+  __shared__ float lds_m[2][NW], lds_s[2][NW], lds_mn[2][NW];
+  __shared__ uint32_t lds_u[2 * NW + 4];
+  __shared__ double lds_d[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t G = gridDim.x;
+  const int nvec = (int)(a.V / EPV);
+  const uint32_t rbytes = (uint32_t)nvec * 16u;
+  const uint32_t voff = (uint32_t)tid * 16u;
+
+  const uint32_t epoch = ld_agent(&a.ws->epoch);
+  const uint32_t tag = epoch + 1u;
+  if (blockIdx.x < a.K) count_and_publish<NT>(a, (int)blockIdx.x, tag, lds_u + 4);
+
+  poll_to_lds(a, tag, lds_u);
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < a.N; row += G) {
+    char* base = a.logits + row * a.ld * ESZ;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(base, rbytes);
+    const int64_t y = a.labels[row];
+    const bool ignored = (y == a.ignore);
+    const bool bad = !ignored && (y < 0 || y >= a.V);
+    u32x4 v[VPL];
+    if (!ignored) buf_load_row<NT, VPL, POL>(v, rs, voff);
+
+    float lse = 0.0f, loss = 0.0f, pcomp = 0.0f;
+    if (!ignored) {
+      const float xy = bad ? 0.0f : T::load1(((const typename T::bits_t*)base)[y]);
+      float m = -INFINITY, mn = INFINITY;
+      pass0_16<T, NT, VPL>(v, nvec, tid, m, mn);
+      int kx = -1, ex = 0;
+      if (!bad) {
+        const int vy = (int)(y / EPV);
+        if (tid == vy % NT) {
+          kx = vy / NT;
+          ex = (int)(y % EPV);
+        }
+      }
+      const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
+      float s = pass1_16<T, NT, VPL>(v, nvec, tid, mc, -INFINITY, -INFINITY, kx, ex);
+      wave_ms(m, s);
+      mn = wave_min(mn);
+      if (lane == 0) {
+        lds_m[par][wid] = m;
+        lds_s[par][wid] = s;
+        lds_mn[par][wid] = mn;
+      }
+      __syncthreads();
+      float M = lds_m[par][0], S_ex = lds_s[par][0], MN = lds_mn[par][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        ms_merge(M, S_ex, lds_m[par][w], lds_s[par][w]);
+        MN = fminf(MN, lds_mn[par][w]);
+      }
+      par ^= 1;
+      if (bad) {
+        lse = loss = pcomp = __builtin_nanf("");
+        buf_fill_row<NT, VPL, POL>(rs, voff, (T::ESZ == 2) ? 0x7fc07fc0u : 0x7fc00000u);
+      } else {
+        const float ey = __builtin_amdgcn_exp2f((xy - M) * kLog2e);
+        const float S = S_ex + ey;
+        lse = M + logf(S);
+        pcomp = S_ex / S;
+        loss = (pcomp >= 0.5f) ? (lse - xy) : log1pf(S_ex / ey);
+        const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+        const float scale = (float)scale_d;
+        const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
+        const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
+        if (grad_mode<T>(scale, tmin) == kFold) {
+          pass2_buf<T, NT, VPL, POL, false>(v, rs, rs, voff, kc, kx, ex);
+        } else {
+          grad_row_generic<T>(base, base, a.V, y, (double)lse, scale_d, (double)kc.gy, tid, NT);
+        }
+      }
+    } else {
+      buf_fill_row<NT, VPL, POL>(rs, voff, 0u);
+    }
+    if (tid == 0) {
+      a.loss_rows[row] = loss;
+      if (a.lse_rows) a.lse_rows[row] = (double)lse;
+      if (a.pcomp_rows) a.pcomp_rows[row] = (double)pcomp;
+      publish_loss(a, row, loss, tag);
+    }
+  }
+  if (blockIdx.x == G - 1) {
     __syncthreads();
     finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
   }
