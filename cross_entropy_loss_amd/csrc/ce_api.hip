@@ -28,6 +28,12 @@ int64_t max_slab(int dtype) { return (int64_t)1024 * 16 * epv(dtype); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Vocabulary split: C slabs of width `width` (C == 1: whole rows on chip).
+// A row that fits on chip is reduced whole in one pass whatever `chunk` is:
+// its workgroup already merges (max, sum) partials of many lanes and waves,
+// a finer partition of the same log-sum-exp merge, and the result differs
+// from a per-slab merge only by rounding.  Wider rows are cut into slabs of
+// width `chunk` (default 65536 16-bit / 32768 fp32 elements) whose partials
+// are merged per row.
 struct Split {
   int64_t width;
   int C;
@@ -35,7 +41,8 @@ struct Split {
 bool make_split(int64_t V, int64_t chunk, int dtype, Split* s) {
   const int64_t cap = max_slab(dtype);
   int64_t w;
-  if (chunk == 0 || chunk >= V) w = (V <= cap) ? V : (dtype == CE_DTYPE_F32 ? 32768 : 65536);
+  if (V <= cap) w = V;
+  else if (chunk == 0 || chunk >= V) w = (dtype == CE_DTYPE_F32) ? 32768 : 65536;
   else w = chunk;
   if (w > cap) return false;
   s->width = w;

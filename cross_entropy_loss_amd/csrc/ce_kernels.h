@@ -365,6 +365,25 @@ __device__ void poll_to_lds(const Args& a, uint32_t tag, uint32_t* lds_u) {
   }
 }
 
+// The same sums when the counts were published by an earlier launch of the
+// call (already complete, so nothing to wait for).  Kernels whose workgroups
+// are not all waited on by the finisher must use this form: a workgroup that
+// polls with the epoch it read could start after the finisher has bumped the
+// epoch and wait for a tag that never comes.
+__device__ void counts_to_lds(const Args& a, uint32_t* lds_u) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  const uint64_t w = (lane < a.K) ? ld_agent(&a.ws->part[lane]) : 0ull;
+  uint32_t c = (uint32_t)(w & 0x7fffffffu);
+  uint32_t b = (uint32_t)((w >> 31) & 1u);
+  c = wave_sum(c);
+  b = wave_or(b);
+  if (lane == 0) {
+    lds_u[0] = c;
+    lds_u[1] = b;
+  }
+}
+
 // A row's loss, published for the finisher (one thread).
 __device__ __forceinline__ void publish_loss(const Args& a, int64_t row, float loss, uint32_t tag) {
   st_agent(&a.slots[row], ((uint64_t)tag << 32) | (uint64_t)__builtin_bit_cast(uint32_t, loss));
@@ -1311,7 +1330,7 @@ __global__ __launch_bounds__(NT) void slab_merge_kernel(Args a) {
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint32_t epoch = ld_agent(&a.ws->epoch);
-  poll_to_lds(a, epoch + 1u, lds_u);
+  counts_to_lds(a, lds_u);  // published by the statistics launch
   if (tid == 0) {
     const int64_t y = a.labels[row];
     RowStats r = {0.0, 0.0, 0.0, false};
@@ -1359,7 +1378,9 @@ __global__ __launch_bounds__(NT) void slab_grad_kernel(Args a) {
       if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
     }
   }
-  poll_to_lds(a, epoch + 1u, lds_u);
+  // published by the statistics launch; slabs c > 0 publish no loss slot, so
+  // the finisher does not wait for them and they must not wait on the epoch
+  counts_to_lds(a, lds_u);
   if (tid == 0 && !ignored) {
     const RowStats r = merge_slabs(a, row);
     lds_r[0] = r.lse;

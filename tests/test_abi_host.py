@@ -44,9 +44,13 @@ def test_abi_version_and_strings(lib):
 
 def test_workspace_bytes(lib):
     whole = lib.ce_workspace_bytes(4096, 32000, 0, _lib.CE_DTYPE_BF16)
-    chunked = lib.ce_workspace_bytes(8192, 128256, 65536, _lib.CE_DTYPE_BF16)
+    # a 128256-wide bf16 row fits on chip: reduced whole, chunk or not
+    fits = lib.ce_workspace_bytes(8192, 128256, 65536, _lib.CE_DTYPE_BF16)
     assert 0 < whole <= 1024 + 4096 * 8 + 256  # header + one tagged loss slot per row
-    assert chunked >= 8192 * 2 * 16 + 8192 * 4
+    assert fits == lib.ce_workspace_bytes(8192, 128256, 0, _lib.CE_DTYPE_BF16) <= 1024 + 8192 * 8 + 256
+    # wider rows are cut into slabs: (max, sum) pairs and the label logit per row
+    chunked = lib.ce_workspace_bytes(8192, 200000, 65536, _lib.CE_DTYPE_BF16)
+    assert chunked >= 8192 * 4 * 16 + 8192 * 4
     auto = lib.ce_workspace_bytes(8, 300000, 0, _lib.CE_DTYPE_BF16)  # > on-chip row: auto-chunked
     assert auto > lib.ce_workspace_bytes(8, 30000, 0, _lib.CE_DTYPE_BF16)
     assert lib.ce_workspace_bytes(-1, 10, 0, 1) == 0
@@ -94,6 +98,7 @@ def forward(lib, **kw):
     (dict(ws=FAKE + 16), _lib.CE_ERR_WORKSPACE),            # workspace must be 256-byte aligned
     (dict(V=300000, ld=300000, chunk=200000), _lib.CE_ERR_UNSUPPORTED),
     (dict(N=8192, V=128256, ld=128256, chunk=65536, ws_bytes=4096), _lib.CE_ERR_WORKSPACE),
+    (dict(N=64, V=200000, ld=200000, chunk=65536, ws_bytes=1024 + 64 * 8 + 256), _lib.CE_ERR_WORKSPACE),
 ])
 def test_fused_rejects(lib, kw, code):
     assert fused(lib, **kw) == code

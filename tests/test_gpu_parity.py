@@ -125,17 +125,52 @@ def test_strided_and_unaligned(dtype, ld, offset):
     check_against_oracle(out, g, bits, p.labels, dtype)
 
 
+@pytest.mark.parametrize("dtype,V,ld,offset", [("bf16", 32001, 32003, 1), ("bf16", 5000, 5000, 3),
+                                               ("f16", 32001, 32011, 5), ("f16", 70001, 70001, 7)])
+def test_split_rows_strided_and_unaligned(dtype, V, ld, offset):
+    # rows cut into pieces whose 16-byte phase differs from piece to piece
+    w = wl.custom(f"split-strided-{dtype}-{V}", 23, 21, V, dtype, 30.0 if dtype == "f16" else 2.0, 0.1)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype, ld=ld, offset=offset)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+    st = g.untyped_storage()
+    buf = torch.empty(0, dtype=torch.int16, device=g.device).set_(st, 0, (st.nbytes() // 2,), (1,))
+    rows = buf[offset: offset + bits.shape[0] * ld].view(bits.shape[0], ld)
+    assert (rows[:, V:] == 0).all() and (buf[:offset] == 0).all() and (buf[offset + bits.shape[0] * ld:] == 0).all(), \
+        "elements outside the rows were written"
+
+
+# rows that fit on chip are reduced whole whatever the chunk; wider rows
+# (beyond 131072 16-bit or 65536 fp32 elements) are cut into slabs of width
+# chunk (0: 65536 / 32768) whose partials are merged
 CHUNKS = [("f32", 1000, c) for c in (1, 7, 128, 999, 1000)] + \
-         [("bf16", 4097, c) for c in (1, 1000, 4096)] + [("f16", 3000, 1024), ("bf16", 70000, 65536)]
+         [("bf16", 4097, c) for c in (1, 1000, 4096)] + [("f16", 3000, 1024), ("bf16", 70000, 65536)] + \
+         [("bf16", 140000, 0), ("bf16", 140001, 50000), ("f16", 200003, 65536), ("f16", 131073, 1),
+          ("f32", 70001, 0), ("f32", 65537, 20000)]
 
 
 @pytest.mark.parametrize("dtype,V,chunk", CHUNKS, ids=[f"{d}-V{v}-c{c}" for d, v, c in CHUNKS])
 def test_chunked(dtype, V, chunk):
-    N = 64 if V <= 1000 else 12
+    N = 64 if V <= 1000 else (12 if V <= 70000 else 6)
     w = wl.custom(f"chunk-{dtype}-{V}", 5, N, V, dtype, 1.0 if dtype == "f32" else 2.0, 0.1)
     bits, p = wl.make(w)
     out, g = run_fused(bits, p.labels, dtype, chunk=chunk)
     check_against_oracle(out, g, bits, p.labels, dtype)
+
+
+def test_slab_calls_leave_no_stale_status():
+    # the slab path's second launch has workgroups the finisher does not wait
+    # for; none of them may leave a status bit behind for the next call
+    w = wl.custom("slab-status", 9, 6, 131073, "f16", 2.0, 0.1)
+    bits, p = wl.make(w)
+    small = wl.custom("slab-status-small", 10, 8, 1000, "f32", 1.0, 0.1)
+    sbits, sp = wl.make(small)
+    for i in range(4):
+        out, g = run_fused(bits, p.labels, "f16", chunk=1)
+        assert int(out["status"].item()) == 0, f"call {i}"
+        out, g = run_fused(sbits, sp.labels, "f32")
+        assert int(out["status"].item()) == 0, f"call {i} (small)"
+    check_against_oracle(out, g, sbits, sp.labels, "f32")
 
 
 def test_no_valid_rows():
@@ -211,9 +246,10 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("dtype,V,chunk", [("bf16", 32000, 0), ("f16", 5000, 0), ("f32", 1000, 0),
-                                           ("bf16", 70000, 32768), ("f32", 3000, 1000)])
+                                           ("bf16", 70000, 32768), ("f32", 3000, 1000), ("bf16", 150001, 65536),
+                                           ("f32", 70001, 0)])
 def test_split_forward_backward(dtype, V, chunk):
-    w = wl.custom("split", 47, 20, V, dtype, 2.0, 0.1)
+    w = wl.custom("split", 47, 20 if V <= 70000 else 6, V, dtype, 2.0, 0.1)
     bits, p = wl.make(w)
     _say(f"[split] dtype={dtype} V={V} chunk={chunk}")
     x = to_device(bits, dtype)
