@@ -220,6 +220,30 @@ __device__ __forceinline__ void wave_ms(F& m, F& s) {
     ms_merge(m, s, m2, s2);
   }
 }
+__device__ __forceinline__ float first_lane(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// Merge of the NW per-wave (max, sum, min) triples a workgroup left in LDS:
+// lane w of every wave takes triple w and the wave reduces them, so the
+// registers hold one triple per lane whatever NW is; every wave takes lane
+// 0's result, so all waves hold the same values.
+template <int NW>
+__device__ __forceinline__ void block_ms(const float* lm, const float* ls, const float* lmn, float& M, float& S,
+                                         float& MN) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY, s = 0.0f, mn = INFINITY;
+  if (lane < NW) {
+    m = lm[lane];
+    s = ls[lane];
+    mn = lmn[lane];
+  }
+  wave_ms(m, s);
+  mn = wave_min(mn);
+  M = first_lane(m);
+  S = first_lane(s);
+  MN = first_lane(mn);
+}
 
 // ---------------------------------------------------------------------------
 // Per-call arguments.
@@ -503,25 +527,33 @@ __device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int t
   return s0 + s1;
 }
 
-// One gradient element of a 16-bit row.  MODE selects the arithmetic:
-//   kFold  g = 2^(x log2e - b), b = lse log2e - log2 s   (s > 0 and finite)
-//   kMul   g = 2^(x log2e - lse log2e) * s               (any s)
-//   kF64   g = exp(x - lse) * s in fp64                  (outputs that may be
-//          subnormal in bf16, where v_exp_f32 would flush below 2^-126)
-enum { kFold = 0, kMul = 1, kF64 = 2 };
+// One gradient element of a 16-bit row: with u = (x - lse) log2e <= 0 and
+// s = dloss / n_valid, g = 2^u s.  MODE selects the arithmetic:
+//   kFold    g = 2^(x log2e - b),  b = lse log2e - log2 s      (s > 0)
+//   kScaled  g = 2^(x log2e - (lse log2e - c)) * (s 2^-c),  c = ilogb(s) + 9
+//   kMul     g = 2^(x log2e - lse log2e) * s                   (other s)
+// v_exp_f32 flushes results below 2^-126 to zero, while bf16 keeps
+// subnormals down to 2^-133.  In kScaled the factor s 2^-c lies in
+// [2^-9, 2^-8), so every output that rounds to a nonzero 16-bit value has
+// its power of two at or above 2^-126 (and at most 2^127 for |s| < 2^118):
+// the flush never decides a result and the product rounds once more to fp32
+// (a subnormal fp32 product is kept; the final 16-bit rounding then differs
+// from a single rounding by at most one unit of the last place).
+enum { kFold = 0, kMul = 1, kScaled = 2 };
+constexpr float kScaledMax = 0x1p118f;  // |s| range served by kScaled
 struct GradConsts {
-  float b;        // kFold exponent offset
-  float lc;       // lse * log2e
-  float scale;    // s
-  double lse_d;   // lse (fp64 path)
-  double scale_d; // s (fp64 path)
-  float gy;       // the label element's gradient, -s (1 - p_y)
+  float b;      // kFold exponent offset
+  float lc;     // lse log2e (kMul)
+  float lcs;    // lse log2e - c (kScaled)
+  float scale;  // s (kMul)
+  float ss;     // s 2^-c (kScaled)
+  float gy;     // the label element's gradient, -s (1 - p_y)
 };
 template <int MODE>
 __device__ __forceinline__ float gelem(float x, const GradConsts& k) {
   if constexpr (MODE == kFold) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.b));
   else if constexpr (MODE == kMul) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.lc)) * k.scale;
-  else return (float)(exp((double)x - k.lse_d) * k.scale_d);
+  else return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.lcs)) * k.ss;
 }
 
 // Next-row prefetch issued from pass 2: once vector k of the current row has
@@ -579,17 +611,20 @@ __device__ __forceinline__ float gscalar(float x, bool is_label, const GradConst
 }
 
 // Picks the pass-2 arithmetic for a row.  tmin: a lower bound of
-// min_j (x_j - lse) log2e over the row (only used for bf16).
+// min_j (x_j - lse) log2e over the row (only used for bf16).  kFold computes
+// 2^t with t = u + log2 s, flushed below 2^-126, which matters only for bf16
+// (its subnormals reach 2^-133); kMul's 2^u is flushed below 2^-126, which
+// matters once |s| exceeds T::kSlowScale.  Those rows take kScaled.  (Scales
+// of 2^118 and beyond, which no loss gradient reaches, keep kFold / kMul.)
 template <typename T>
 __device__ __forceinline__ int grad_mode(float scale, float tmin) {
-  const bool pos = scale > 0.0f && scale <= 3.0e38f;
-  if (pos) {
-    // folded: 2^t with t = (x - lse) log2e + log2 s is flushed below 2^-126,
-    // which matters only for bf16 (its subnormals reach 2^-133)
-    if (T::kBF && tmin + log2f(scale) < -125.0f) return kF64;
+  const float as = fabsf(scale);
+  const bool scalable = as > 0.0f && as < kScaledMax;  // false for NaN
+  if (scale > 0.0f && scale <= 3.0e38f) {
+    if (T::kBF && scalable && tmin + log2f(scale) < -125.0f) return kScaled;
     return kFold;
   }
-  if (fabsf(scale) > T::kSlowScale && (!T::kBF || tmin < -125.0f)) return kF64;
+  if (scalable && as > T::kSlowScale && (!T::kBF || tmin < -125.0f)) return kScaled;
   return kMul;
 }
 
@@ -598,26 +633,13 @@ __device__ __forceinline__ GradConsts grad_consts(float lse, float scale, double
   GradConsts k;
   k.lc = lse * kLog2e;
   k.b = k.lc - log2f(scale);  // used only when scale > 0
+  const float as = fabsf(scale);
+  const int c = (as > 0.0f && as < kScaledMax) ? ilogbf(scale) + 9 : 0;
+  k.lcs = k.lc - (float)c;
+  k.ss = ldexpf(scale, -c);
   k.scale = scale;
-  k.lse_d = (double)lse;
-  k.scale_d = scale_d;
   k.gy = (float)(-scale_d * pcomp);
   return k;
-}
-
-// Gradient of one row in fp64, read from memory (rows whose scale is not a
-// positive finite number, and bf16 rows whose outputs may be subnormal, where
-// v_exp_f32 would flush).  Out of line: it holds none of the caller's staged
-// registers.  Reads each element before writing it, lane by lane, so it may
-// run in place.
-template <typename T>
-__device__ __forceinline__ void grad_row_generic(const char* xrow, char* grow, int64_t V, int64_t y, double lse,
-                                              double scale, double gy, int tid, int nt) {
-  typedef typename T::bits_t B;
-  for (int64_t j = tid; j < V; j += nt) {
-    const double gd = (j == y) ? gy : exp((double)T::load1(((const B*)xrow)[j]) - lse) * scale;
-    ((B*)grow)[j] = T::store1((float)gd);
-  }
 }
 
 // Writes NaN over a row whose label is out of range.
@@ -656,9 +678,9 @@ __device__ __forceinline__ void grad_row_16(u32x4 (&v)[VPL], int nvec, int tid, 
     gh = gscalar<T, kMul>(xh, own.head > 0, kc);
     gt = gscalar<T, kMul>(xt, own.tail > 0, kc);
   } else {
-    pass2_16<T, NT, VPL, POL, kF64>(v, nvec, tid, gbody, kc, own, pf);
-    gh = gscalar<T, kF64>(xh, own.head > 0, kc);
-    gt = gscalar<T, kF64>(xt, own.tail > 0, kc);
+    pass2_16<T, NT, VPL, POL, kScaled>(v, nvec, tid, gbody, kc, own, pf);
+    gh = gscalar<T, kScaled>(xh, own.head > 0, kc);
+    gt = gscalar<T, kScaled>(xt, own.tail > 0, kc);
   }
   if (ph) *ph = T::store1(gh);
   if (pt) *pt = T::store1(gt);
@@ -680,17 +702,20 @@ __device__ __forceinline__ float lane_min_16(const u32x4 (&v)[VPL], int nvec, in
 }
 
 // grad_mode for a workgroup whose lanes each know only their own minimum:
-// the fp64 fallback is agreed with one barrier (bf16 only).
+// kScaled is agreed with one barrier (bf16 only).
 template <typename T>
 __device__ __forceinline__ int block_grad_mode(float scale, float tmin_lane) {
+  const float as = fabsf(scale);
   const bool pos = scale > 0.0f && scale <= 3.0e38f;
+  const bool scalable = as > 0.0f && as < kScaledMax;
   if constexpr (T::kBF) {
-    const bool lane = pos ? (tmin_lane + log2f(scale) < -125.0f) : (fabsf(scale) > T::kSlowScale && tmin_lane < -125.0f);
-    if (__syncthreads_or(lane ? 1 : 0)) return kF64;
+    const bool lane = pos ? (tmin_lane + log2f(scale) < -125.0f) : (as > T::kSlowScale && tmin_lane < -125.0f);
+    const int any = __syncthreads_or(lane ? 1 : 0);
+    if (scalable && any) return kScaled;
     return pos ? kFold : kMul;
   } else {
     if (pos) return kFold;
-    return fabsf(scale) > T::kSlowScale ? kF64 : kMul;
+    return (scalable && as > T::kSlowScale) ? kScaled : kMul;
   }
 }
 
@@ -718,10 +743,20 @@ __device__ __forceinline__ void zero_row(char* gbase, const Geom& g, int tid, in
 // persistent variant that loops over rows measured no faster at these row
 // sizes: the hardware refills a finished workgroup's slot within ~2 us.)
 // ---------------------------------------------------------------------------
-// At least 4 waves per SIMD: a 256-lane row workgroup stages 64 KB in 64
-// VGPRs and must leave room for four such rows per CU.
+// Waves per SIMD the register budget must allow: 8 for 512- and 1024-lane
+// shapes of at most 8 vectors per lane (64 VGPRs: four 512-lane rows per
+// CU), 4 otherwise (128 VGPRs).  Without a bound the compiler may take up to
+// 256 VGPRs for a 512-lane shape and fit one row per CU.
+template <int NT, int VPL>
+constexpr int row_min_waves() { return (NT >= 512 && VPL <= 8) ? 8 : 4; }
+// The statistics pass holds no gradient state: 64 VGPRs for up to 8 vectors
+// per lane.  (With a 128-VGPR budget the scheduler has been seen to build up
+// more than 128 live values in the 256 x 8 shape and spill.)
+template <int VPL>
+constexpr int stats_min_waves() { return VPL <= 8 ? 8 : 4; }
+
 template <typename T, int NT, int VPL, int POL, bool FUSED>
-__global__ __launch_bounds__(NT, 4) void row_kernel_16(Args a) {
+__global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
   typedef typename T::bits_t B;
   __shared__ float lds_m[NW], lds_s[NW], lds_mn[NW];
@@ -773,12 +808,8 @@ __global__ __launch_bounds__(NT, 4) void row_kernel_16(Args a) {
       lds_mn[wid] = mn;
     }
     __syncthreads();
-    float M = lds_m[0], S_ex = lds_s[0], MN = lds_mn[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      ms_merge(M, S_ex, lds_m[w], lds_s[w]);
-      MN = fminf(MN, lds_mn[w]);
-    }
+    float M, S_ex, MN;
+    block_ms<NW>(lds_m, lds_s, lds_mn, M, S_ex, MN);
     if (badlab) {
       lse = loss = pcomp = __builtin_nanf("");
     } else {
@@ -799,15 +830,10 @@ __global__ __launch_bounds__(NT, 4) void row_kernel_16(Args a) {
         // lower bound of (x - lse) log2e over the row (bf16 lane minima are
         // lower bounds within one bf16 ulp; widen by 2^-7 relative)
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
-        if (grad_mode<T>(scale, tmin) == kFold) {
-          pass2_16<T, NT, VPL, POL, kFold>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), kc, own,
-                                           Prefetch{nullptr, 0});
-          if (has_h) ((B*)gbase)[tid] = T::store1(gscalar<T, kFold>(xh, own.head > 0, kc));
-          if (has_t)
-            ((B*)gbase)[g.head + (int64_t)g.nvec * EPV + tid] = T::store1(gscalar<T, kFold>(xt, own.tail > 0, kc));
-        } else {
-          grad_row_generic<T>(rbase, gbase, a.V, y, (double)lse, scale_d, (double)kc.gy, tid, NT);
-        }
+        const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
+        grad_row_16<T, NT, VPL, POL>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), grad_mode<T>(scale, tmin), kc,
+                                     own, xh, xt, has_h ? (B*)gbase + tid : nullptr,
+                                     has_t ? (B*)gbase + jt : nullptr);
       }
     }
   } else {
@@ -847,6 +873,21 @@ constexpr int aux_load() { return (POL & 1) ? 2 : 0; }
 template <int POL>
 constexpr int aux_store() { return (POL & 2) ? 2 : 0; }
 
+// A 128-bit buffer store.  The hardware reads a store's data registers after
+// the instruction issues, and a VALU write to them must wait two cycles; the
+// compiler leaves no such gap when the store's soffset is a register (it
+// assumes the hazard only exists without one), and a gradient vector built in
+// the same registers right after a store then reached memory in part.  Two
+// wait states follow every store here, kept in place by scheduling barriers.
+template <int AUX>
+__device__ __forceinline__ void buf_store(u32x4 v, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v), rs, voff, soff,
+                                         AUX);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int NT, int VPL, int POL>
 __device__ __forceinline__ void buf_load_row(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
 #pragma unroll
@@ -857,15 +898,13 @@ template <int NT, int VPL, int POL>
 __device__ __forceinline__ void buf_fill_row(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t word) {
   const u32x4 z = {word, word, word, word};
 #pragma unroll
-  for (int k = 0; k < VPL; ++k)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, z), rs, voff,
-                                           k * NT * 16, aux_store<POL>());
+  for (int k = 0; k < VPL; ++k) buf_store<aux_store<POL>()>(z, rs, voff, k * NT * 16);
 }
 
-// pass 2 (folded scale) on buffer stores, with the next row's loads issued
-// into the registers each vector frees.  Lanes past the row compute garbage
-// that their dropped stores discard.
-template <typename T, int NT, int VPL, int POL, bool PF>
+// pass 2 on buffer stores, optionally with the next row's loads issued into
+// the registers each vector frees.  Lanes past the row compute garbage that
+// their dropped stores discard.
+template <typename T, int NT, int VPL, int POL, bool PF, int MODE>
 __device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t out, __amdgpu_buffer_rsrc_t nxt,
                                           uint32_t voff, const GradConsts& kc, int kx, int ex) {
 #pragma unroll
@@ -873,8 +912,8 @@ __device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_
     float gv[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      gv[2 * d] = gelem<kFold>(T::lo(v[k][d]), kc);
-      gv[2 * d + 1] = gelem<kFold>(T::hi(v[k][d]), kc);
+      gv[2 * d] = gelem<MODE>(T::lo(v[k][d]), kc);
+      gv[2 * d + 1] = gelem<MODE>(T::hi(v[k][d]), kc);
     }
     if (k == kx) {
 #pragma unroll
@@ -883,8 +922,7 @@ __device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_
     u32x4 o;
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, o), out, voff,
-                                           k * NT * 16, aux_store<POL>());
+    buf_store<aux_store<POL>()>(o, out, voff, k * NT * 16);
     if constexpr (PF) {
       __builtin_amdgcn_sched_barrier(0);
       v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nxt, voff, k * NT * 16, aux_load<POL>()));
@@ -942,12 +980,8 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
         lds_mn[par][wid] = mn;
       }
       __syncthreads();
-      float M = lds_m[par][0], S_ex = lds_s[par][0], MN = lds_mn[par][0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        ms_merge(M, S_ex, lds_m[par][w], lds_s[par][w]);
-        MN = fminf(MN, lds_mn[par][w]);
-      }
+      float M, S_ex, MN;
+      block_ms<NW>(lds_m[par], lds_s[par], lds_mn[par], M, S_ex, MN);
       par ^= 1;
       if (bad) {
         lse = loss = pcomp = __builtin_nanf("");
@@ -962,11 +996,10 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
         const float scale = (float)scale_d;
         const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
-        if (grad_mode<T>(scale, tmin) == kFold) {
-          pass2_buf<T, NT, VPL, POL, false>(v, rs, rs, voff, kc, kx, ex);
-        } else {
-          grad_row_generic<T>(base, base, a.V, y, (double)lse, scale_d, (double)kc.gy, tid, NT);
-        }
+        const int mode = grad_mode<T>(scale, tmin);
+        if (mode == kFold) pass2_buf<T, NT, VPL, POL, false, kFold>(v, rs, rs, voff, kc, kx, ex);
+        else if (mode == kScaled) pass2_buf<T, NT, VPL, POL, false, kScaled>(v, rs, rs, voff, kc, kx, ex);
+        else pass2_buf<T, NT, VPL, POL, false, kMul>(v, rs, rs, voff, kc, kx, ex);
       }
     } else {
       buf_fill_row<NT, VPL, POL>(rs, voff, 0u);
@@ -1205,7 +1238,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
 // sum.  blockIdx.x = row * C + c; slab c covers elements [c*chunk, ...).
 // ---------------------------------------------------------------------------
 template <typename T, int NT, int VPL, int POL>
-__global__ __launch_bounds__(NT) void slab_stats_kernel(Args a) {
+__global__ __launch_bounds__(NT, (stats_min_waves<VPL>())) void slab_stats_kernel(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
   typedef typename T::acc_t A;
   typedef typename T::bits_t B;
@@ -1248,13 +1281,8 @@ __global__ __launch_bounds__(NT) void slab_stats_kernel(Args a) {
     pass0_16<T, NT, VPL>(v, g.nvec, tid, mf, mn);
     if (own.head > 0) xh = -INFINITY;
     if (own.tail > 0) xt = -INFINITY;
-    if (own.k >= 0) {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k)
-        if (k == own.k) T::kill(v[k], own.e);
-    }
     const float mc = (mf == -INFINITY) ? 0.0f : mf * kLog2e;
-    s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh, xt);
+    s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh, xt, own.k, own.e);
     m = mf;
   } else {
     float mf = fmaxf(xh, xt);
@@ -1265,18 +1293,16 @@ __global__ __launch_bounds__(NT) void slab_stats_kernel(Args a) {
         for (int d = 0; d < 4; ++d) mf = fmaxf(mf, as<float>(v[k][d]));
     if (own.head > 0) xh = -INFINITY;
     if (own.tail > 0) xt = -INFINITY;
-    if (own.k >= 0) {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k)
-        if (k == own.k) T::kill(v[k], own.e);
-    }
     const double mm = (mf == -INFINITY) ? 0.0 : (double)mf;
     s = exp((double)xh - mm) + exp((double)xt - mm);
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
       if (k * NT + tid < g.nvec)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) s += exp((double)as<float>(v[k][d]) - mm);
+        for (int d = 0; d < 4; ++d) {
+          const double e = exp((double)as<float>(v[k][d]) - mm);
+          s += (k == own.k && d == own.e) ? 0.0 : e;  // the label is left out
+        }
     m = mf;
   }
   wave_ms(m, s);
@@ -1352,7 +1378,7 @@ __global__ __launch_bounds__(NT) void slab_merge_kernel(Args a) {
 // the mean at the end.  blockIdx.x = row * C + c.
 // ---------------------------------------------------------------------------
 template <typename T, int NT, int VPL, int POL>
-__global__ __launch_bounds__(NT) void slab_grad_kernel(Args a) {
+__global__ __launch_bounds__(NT, 4) void slab_grad_kernel(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
   typedef typename T::bits_t B;
   __shared__ uint32_t lds_u[2 * NW + 4];

@@ -235,6 +235,49 @@ def test_wide_rows_subnormal_outputs(dtype, sigma, n):
     check_against_oracle(out, g, bits, p.labels, dtype)
 
 
+# every pass-2 arithmetic (folded scale, scaled power of two for outputs in
+# the subnormal range, plain product) through every kernel family: whole rows,
+# the persistent kernel for wide aligned rows, slabs, and the split backward
+MODES = [("bf16", 2000, 40.0, 5, 1.0), ("bf16", 2000, 40.0, 5, -3.0), ("bf16", 2000, 2.0, 5, -3.0),
+         ("bf16", 128000, 40.0, 3, 1.0), ("bf16", 128000, 40.0, 3, -3.0), ("bf16", 140000, 40.0, 3, -3.0),
+         ("f16", 3000, 30.0, 8, -1e32), ("f16", 3000, 30.0, 8, 1e32), ("f16", 130000, 30.0, 3, -1e32)]
+
+
+@pytest.mark.parametrize("dtype,V,sigma,n,dloss", MODES, ids=[f"{d}-V{v}-s{s:g}-dl{dl:g}" for d, v, s, n, dl in MODES])
+def test_gradient_modes(dtype, V, sigma, n, dloss):
+    w = wl.custom("modes", 43, n, V, dtype, sigma, 0.0)
+    bits, p = wl.make(w)
+    out, g = run_fused(bits, p.labels, dtype, dloss=dloss)
+    check_against_oracle(out, g, bits, p.labels, dtype, dloss=dloss)
+    x = to_device(bits, dtype)
+    y = torch.from_numpy(p.labels).cuda()
+    dl = torch.tensor([dloss], dtype=torch.float32, device="cuda")
+    f = ce.ce_forward(x, y)
+    grad = ce.ce_backward(x, y, f["lse_rows"], f["pcomp_rows"], f["n_valid"], dl)
+    torch.cuda.synchronize()
+    check_against_oracle(f, grad, bits, p.labels, dtype, dloss=dloss)
+
+
+def test_wide_rows_repeated_calls():
+    # the persistent buffer-store kernel (rows of 128256 bf16 elements): every
+    # call must reproduce the oracle and the first call bit for bit (its store
+    # data registers are rewritten right after each store)
+    w = wl.WORKLOADS[4]
+    p = wl.plan(w)
+    rows = np.arange(96)
+    bits = wl.logits(w, rows, p)
+    labels = p.labels[rows]
+    first = None
+    for i in range(6):
+        out, g = run_fused(bits, labels, w.dtype, dloss=w.dloss)
+        gb = to_host_bits(g, w.dtype)
+        if first is None:
+            check_against_oracle(out, g, bits, labels, w.dtype, dloss=w.dloss)
+            first = gb
+        else:
+            assert (gb == first).all(), f"call {i} differs from call 0"
+
+
 def test_deterministic():
     w = wl.custom("det", 43, 300, 32000, "bf16", 2.0, 0.05)
     bits, p = wl.make(w)
