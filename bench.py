@@ -118,9 +118,12 @@ def profile_summary(d: str, workload: int) -> None:
     lines = [f"# rocprofv3 summary: fused cross-entropy forward+backward, workload {w.name}",
              f"# N={w.N} V={w.V} dtype={w.dtype} chunk={w.chunk}; kernel sources sha {kernel_sha()}",
              "# commands (from the repository root):",
-             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- python bench.py --steps 10 --no-cpu-baseline",
-             "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- python bench.py --steps 5 --no-cpu-baseline --calibrate",
-             "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- python bench.py --steps 5 --no-cpu-baseline --calibrate",
+             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
+             f"python bench.py --workload {workload} --steps 10 --no-cpu-baseline",
+             "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- "
+             f"python bench.py --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
+             "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- "
+             f"python bench.py --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
              f"#   python bench.py --profile-summary D --workload {workload}", ""]
     ce_names = ("row_kernel", "row_fused", "slab_", "grad_kernel")
     dominant = None
