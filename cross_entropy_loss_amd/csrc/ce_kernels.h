@@ -224,26 +224,79 @@ __device__ __forceinline__ float first_lane(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
-// Merge of the NW per-wave (max, sum, min) triples a workgroup left in LDS:
-// lane w of every wave takes triple w and the wave reduces them, so the
-// registers hold one triple per lane whatever NW is; every wave takes lane
-// 0's result, so all waves hold the same values.
-template <int NW>
-__device__ __forceinline__ void block_ms(const float* lm, const float* ls, const float* lmn, float& M, float& S,
-                                         float& MN) {
-  const int lane = threadIdx.x & 63;
-  float m = -INFINITY, s = 0.0f, mn = INFINITY;
-  if (lane < NW) {
-    m = lm[lane];
-    s = ls[lane];
-    mn = lmn[lane];
-  }
-  wave_ms(m, s);
-  mn = wave_min(mn);
-  M = first_lane(m);
-  S = first_lane(s);
-  MN = first_lane(mn);
+// Reductions on DPP lane moves (no LDS traffic).  A step combines each lane
+// with the lane a DPP control selects; lanes a row mask leaves out combine
+// with the identity.  After quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror
+// and row_mirror every lane of a 16-lane row holds the row's result;
+// row_bcast15 (rows 1, 3) and row_bcast31 (rows 2, 3) then leave the
+// wave's result in lane 63.
+struct OpMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+  __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct OpAdd {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+template <int CTRL, int ROWS, typename Op>
+__device__ __forceinline__ float dpp_step(float v, float ident, Op op) {
+  const int t = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident), __builtin_bit_cast(int, v), CTRL, ROWS,
+                                            0xf, false);
+  return op(v, __builtin_bit_cast(float, t));
 }
+// Result of the first N lanes (N = 1, 2, 4, 8 or 16) in each of them.
+template <int N, typename Op>
+__device__ __forceinline__ float row_reduce(float v, float ident, Op op) {
+  if constexpr (N >= 2) v = dpp_step<0xb1, 0xf>(v, ident, op);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v = dpp_step<0x4e, 0xf>(v, ident, op);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v = dpp_step<0x141, 0xf>(v, ident, op);  // row_half_mirror
+  if constexpr (N >= 16) v = dpp_step<0x140, 0xf>(v, ident, op); // row_mirror
+  return v;
+}
+// Result of the whole wave, the same in every lane.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, float ident, Op op) {
+  v = row_reduce<16>(v, ident, op);
+  v = dpp_step<0x142, 0xa>(v, ident, op);  // row_bcast15
+  v = dpp_step<0x143, 0xc>(v, ident, op);  // row_bcast31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Row statistics of a workgroup from each lane's (max m, sum s relative to
+// m, min mn): every wave reduces its maxima, rescales each lane's sum once
+// and adds, then the NW wave triples (LDS) are reduced the same way in the
+// first NW lanes of every wave, so all waves hold the same M, S, MN.
+template <int NW>
+__device__ __forceinline__ void row_stats(float m, float s, float mn, float* lm, float* ls, float* lmn, float& M,
+                                          float& S, float& MN) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const float mw = wave_reduce(m, -INFINITY, OpMax());
+  float sw = (m == -INFINITY) ? 0.0f : s * __builtin_amdgcn_exp2f((m - mw) * kLog2e);
+  sw = wave_reduce(sw, 0.0f, OpAdd());
+  const float nw = wave_reduce(mn, INFINITY, OpMin());
+  if (lane == 0) {
+    lm[wid] = mw;
+    ls[wid] = sw;
+    lmn[wid] = nw;
+  }
+  __syncthreads();
+  float pm = -INFINITY, ps = 0.0f, pn = INFINITY;
+  if (lane < NW) {
+    pm = lm[lane];
+    ps = ls[lane];
+    pn = lmn[lane];
+  }
+  const float mb = row_reduce<NW>(pm, -INFINITY, OpMax());
+  ps = (pm == -INFINITY) ? 0.0f : ps * __builtin_amdgcn_exp2f((pm - mb) * kLog2e);
+  ps = row_reduce<NW>(ps, 0.0f, OpAdd());
+  pn = row_reduce<NW>(pn, INFINITY, OpMin());
+  M = first_lane(mb);
+  S = first_lane(ps);
+  MN = first_lane(pn);
+}
+
+
 
 // ---------------------------------------------------------------------------
 // Per-call arguments.
@@ -799,17 +852,9 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
     // lane that holds it); the staged data itself is not modified
     const float xh1 = (own.head > 0) ? -INFINITY : xh, xt1 = (own.tail > 0) ? -INFINITY : xt;
     const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-    float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh1, xt1, own.k, own.e);
-    wave_ms(m, s);
-    mn = wave_min(mn);
-    if (lane == 0) {
-      lds_m[wid] = m;
-      lds_s[wid] = s;
-      lds_mn[wid] = mn;
-    }
-    __syncthreads();
+    const float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh1, xt1, own.k, own.e);
     float M, S_ex, MN;
-    block_ms<NW>(lds_m, lds_s, lds_mn, M, S_ex, MN);
+    row_stats<NW>(m, s, mn, lds_m, lds_s, lds_mn, M, S_ex, MN);
     if (badlab) {
       lse = loss = pcomp = __builtin_nanf("");
     } else {
@@ -971,17 +1016,9 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
         }
       }
       const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-      float s = pass1_16<T, NT, VPL>(v, nvec, tid, mc, -INFINITY, -INFINITY, kx, ex);
-      wave_ms(m, s);
-      mn = wave_min(mn);
-      if (lane == 0) {
-        lds_m[par][wid] = m;
-        lds_s[par][wid] = s;
-        lds_mn[par][wid] = mn;
-      }
-      __syncthreads();
+      const float s = pass1_16<T, NT, VPL>(v, nvec, tid, mc, -INFINITY, -INFINITY, kx, ex);
       float M, S_ex, MN;
-      block_ms<NW>(lds_m[par], lds_s[par], lds_mn[par], M, S_ex, MN);
+      row_stats<NW>(m, s, mn, lds_m[par], lds_s[par], lds_mn[par], M, S_ex, MN);
       par ^= 1;
       if (bad) {
         lse = loss = pcomp = __builtin_nanf("");
