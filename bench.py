@@ -20,9 +20,11 @@ Profiling (rocprofv3 databases -> profiles/ summaries):
     rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- python bench.py --steps 5 --no-cpu-baseline --calibrate
     rocprofv3 --pmc WRITE_SIZE -d D -o write -- python bench.py --steps 5 --no-cpu-baseline --calibrate
     python bench.py --profile-summary D
---calibrate also runs a plain copy of the logits' size with the kernels'
-16-byte nontemporal loads and stores: the counters' reading of that copy
-gives the factor that turns FETCH_SIZE / WRITE_SIZE into bytes.
+Every run also times a plain copy of the logits' size with the kernels' 16-byte
+nontemporal loads and stores under the same protocol (roofline.copy_ceiling,
+the attainable read + write rate); under the --calibrate runs the counters'
+reading of that copy gives the factor that turns FETCH_SIZE / WRITE_SIZE into
+bytes.
 """
 from __future__ import annotations
 
@@ -73,27 +75,46 @@ def measured_traffic(name: str):
     return c.get("traffic_bytes")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, bits, labels, max_seconds=20.0, min_seconds=5.0):
     """The float64 oracle (forward + backward of every sampled row) on the host
     cores: a bounded sample of the workload's rows, repeated until at least
-    min_seconds of work so the rate is stable."""
+    min_seconds of work so the rate is stable; then the same on one thread
+    (a smaller sample, about 2 s)."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
     n = int((labels != -100).sum())
-    t0 = time.perf_counter()
-    oracle.rows(bits[:64], labels[:64], w.dtype, w.dloss / n, threads=threads)
-    per_row = (time.perf_counter() - t0) / 64
-    rows = int(min(w.N, max(64, max_seconds / 2 / max(per_row, 1e-9))))
-    done, t0 = 0, time.perf_counter()
-    while True:
-        oracle.rows(bits[:rows], labels[:rows], w.dtype, w.dloss / n, threads=threads)
-        done += rows
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or dt >= max_seconds:
-            break
-    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {w.N} rows of {w.name}, {done // rows} passes: float64 forward + "
-                      f"backward, {threads} threads, {dt:.2f} s"}
+
+    def rate(nthreads, budget_max, budget_min):
+        t0 = time.perf_counter()
+        oracle.rows(bits[:16], labels[:16], w.dtype, w.dloss / n, threads=nthreads)
+        per_row = (time.perf_counter() - t0) / 16
+        rows = int(min(w.N, max(16, budget_max / 2 / max(per_row, 1e-9))))
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.rows(bits[:rows], labels[:rows], w.dtype, w.dloss / n, threads=nthreads)
+            done += rows
+            dt = time.perf_counter() - t0
+            if dt >= budget_min or dt >= budget_max:
+                return done / dt, rows, done // rows, dt
+
+    v, rows, passes, dt = rate(threads, max_seconds, min_seconds)
+    v1, rows1, _, dt1 = rate(1, 4.0, 2.0)
+    row_bytes = 2 * w.V * w.elem_bytes
+    return {"value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.N} rows of {w.name}, {passes} passes: float64 forward + "
+                      f"backward, {threads} threads, {dt:.2f} s; one thread: first {rows1} rows, {dt1:.2f} s",
+            "value_1thread": v1, "gbs": v * row_bytes / 1e9, "cpu": cpu_model(), "nproc": os.cpu_count()}
 
 
 def _db_rows(path, sql):
@@ -237,18 +258,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
-    if args.calibrate:
-        import ctypes
-        calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
-        calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        nbytes = pristine.numel() * pristine.element_size()
-        for _ in range(3):
-            flush.fill_(0)
-            rc = calib.ce_calib_copy(ctypes.c_void_p(pristine.data_ptr()), ctypes.c_void_p(work.data_ptr()), nbytes,
-                                     ctypes.c_void_p(stream.cuda_stream))
-            if rc:
-                raise SystemExit(f"calibration copy failed: {rc}")
+    # the measured ceiling: a plain copy of the logits' size (the same 16-byte
+    # nontemporal loads and stores) under the same protocol; with --calibrate
+    # its counter readings also scale FETCH_SIZE / WRITE_SIZE
+    import ctypes
+    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
+    calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    nbytes = pristine.numel() * pristine.element_size()
+    cms = []
+    for i in range(3 if args.calibrate else 7):
+        flush.fill_(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = calib.ce_calib_copy(ctypes.c_void_p(pristine.data_ptr()), ctypes.c_void_p(work.data_ptr()), nbytes,
+                                 ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc:
+            raise SystemExit(f"calibration copy failed: {rc}")
         torch.cuda.synchronize()
+        cms.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * nbytes / (float(np.median(cms[1:])) * 1e-3) / 1e9
     st = int(out["status"].item())
     if st != 0:
         raise SystemExit(f"kernel status {st:#x}")
@@ -271,11 +300,14 @@ def main():
         "config": {"workload": w.name, "rows": w.N, "vocab": w.V, "logits_dtype": w.dtype,
                    "chunk": w.chunk, "n_valid": int((labels != -100).sum()), "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(f"ce_fused_{w.name}")},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(f"ce_fused_{w.name}"),
+                     "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "timing": {"ms_p10": float(np.percentile(ms, 10)), "ms_median": float(np.median(ms)),
                    "ms_p90": float(np.percentile(ms, 90)), "algorithmic_bytes": abytes,
                    "wall_ms_per_step_incl_restore_and_flush": wall / args.steps * 1e3,
-                   "kernel_sha": kernel_sha()},
+                   "kernel_sha": kernel_sha(),
+                   "inputs_sha256": {"logits": hashlib.sha256(bits.tobytes()).hexdigest(),
+                                     "labels": hashlib.sha256(labels.tobytes()).hexdigest()}},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, bits, labels)
