@@ -200,6 +200,81 @@ def profile_summary(d: str, workload: int) -> None:
     print("\n".join(lines))
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense, AMD published
+
+
+def bench_linear(args) -> None:
+    """LM-head projection + cross-entropy, forward and backward (ce_linear_fwd_bwd):
+    one step = one call over the whole batch with the hidden states and weight
+    resident in HBM; L2 and MALL flushed before each step.  Roofline: the call
+    is dominated by its three GEMMs (6 N H V flops), priced against the MFMA
+    peak of the input format."""
+    import torch
+    import cross_entropy_loss_amd as ce
+    import workloads as wl
+    lw = wl.LINEAR_WORKLOADS[args.workload if args.workload in wl.LINEAR_WORKLOADS else 1]
+    h, w, y = wl.linear_inputs(lw)
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[lw.dtype]
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16) if lw.elem_bytes == 2 else a.view(np.int32)).to(dev).view(tdt)
+
+    hd, wd = to_dev(h), to_dev(w)
+    yd = torch.from_numpy(y).to(dev)
+    dl = torch.tensor([lw.dloss], dtype=torch.float32, device=dev)
+    ws = ce.Workspace(dev, ce.ce_linear_workspace_bytes(lw.N, lw.H, lw.V, lw.chunk_rows, tdt))
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = None
+    for i in range(args.warmup):
+        flush.fill_(i)
+        out = ce.ce_linear_fwd_bwd(hd, wd, yd, chunk_rows=lw.chunk_rows, dloss=dl, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(args.warmup + i)
+        ev[i][0].record(stream)
+        out = ce.ce_linear_fwd_bwd(hd, wd, yd, chunk_rows=lw.chunk_rows, dloss=dl, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = int(out["status"].item())
+    if st != 0:
+        raise SystemExit(f"kernel status {st:#x}")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_mean = float(ms.mean())
+    flops = 6.0 * lw.N * lw.H * lw.V
+    tf = flops / (ms_mean * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[lw.dtype]
+    rec = {
+        "metric": f"LM-head + CE fwd+bwd tokens/s, N={lw.N} H={lw.H} V={lw.V} {lw.dtype}",
+        "value": lw.N / (ms_mean * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_mean, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": lw.dtype, "data": "synthetic",
+        "config": {"workload": lw.name, "rows": lw.N, "hidden": lw.H, "vocab": lw.V, "chunk_rows": lw.chunk_rows,
+                   "n_valid": int((y != -100).sum()), "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                     "traffic": None},
+        "timing": {"ms_p10": float(np.percentile(ms, 10)), "ms_median": float(np.median(ms)),
+                   "ms_p90": float(np.percentile(ms, 90)), "flops": flops,
+                   "wall_ms_per_step_incl_flush": wall / args.steps * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import linear as olin
+        rows, done, t0 = 16, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            olin.linear_cross_entropy(h[:rows], w, y[:rows], lw.dtype, dloss=lw.dloss)
+            done += rows
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done / dt, "unit": "tokens/s", "cores": min(16, os.cpu_count() or 1),
+                               "kind": "oracle",
+                               "sample": f"first {rows} rows of {lw.name} against the whole weight, float64 "
+                                         f"forward + both gradients (numpy BLAS), {done // rows} passes, {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +284,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR")
+    ap.add_argument("--op", choices=["ce", "linear"], default="ce",
+                    help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy")
     args = ap.parse_args()
     if args.profile_summary:
         profile_summary(args.profile_summary, args.workload)
@@ -217,6 +294,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.op == "linear":
+        bench_linear(args)
+        return
 
     import torch
     import cross_entropy_loss_amd as ce

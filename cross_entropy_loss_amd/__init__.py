@@ -22,6 +22,7 @@ from ._lib import (CE_STATUS_LABEL_RANGE, CE_STATUS_SYNC_TIMEOUT, CeError)  # no
 __all__ = [
     "ce_workspace_bytes", "ce_workspace_init", "Workspace", "ce_forward", "ce_backward",
     "ce_fwd_bwd_inplace", "cross_entropy", "FastCrossEntropyLoss", "CeError",
+    "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
 ]
 
 _DTYPES = {torch.float32: _lib.CE_DTYPE_F32, torch.bfloat16: _lib.CE_DTYPE_BF16,
@@ -183,6 +184,53 @@ def ce_fwd_bwd_inplace(logits: torch.Tensor, labels: torch.Tensor, ignore_index:
         _ptr(out["loss_rows"]), _ptr(out["lse_rows"]), _ptr(out["pcomp_rows"]), _ptr(out["n_valid"]),
         _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(logits.device))
     _lib.check(rc, "ce_fwd_bwd_inplace")
+    return out
+
+
+def ce_linear_workspace_bytes(n_rows: int, hidden: int, vocab: int, chunk_rows: int, dtype: torch.dtype) -> int:
+    n = _lib.load().ce_linear_workspace_bytes(n_rows, hidden, vocab, chunk_rows, _DTYPES[dtype])
+    if n == 0:
+        raise ValueError("no LM-head workspace size for these arguments")
+    return int(n)
+
+
+def _matrix(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+        raise ValueError(f"{name} must be a 2-D GPU tensor with contiguous rows")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def ce_linear_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+                      chunk_rows: int = 0, dloss: torch.Tensor | None = None, workspace: Workspace | None = None,
+                      want_grad_hidden: bool = True, want_grad_weight: bool = True) -> dict:
+    """LM-head projection + cross-entropy, forward and backward, token-chunked:
+    loss_mean, loss_rows, n_valid, status and (when asked for) grad_hidden,
+    grad_weight of dloss * L."""
+    N, H, ldh = _matrix(hidden, "hidden")
+    V, H2, ldw = _matrix(weight, "weight")
+    if H2 != H or weight.dtype != hidden.dtype or weight.device != hidden.device:
+        raise ValueError("weight must be [vocab, hidden] of the hidden states' dtype and device")
+    dt = _dtype_code(hidden)
+    labels = _labels(labels, N, hidden.device)
+    if dloss is not None and (dloss.dtype != torch.float32 or dloss.numel() != 1):
+        raise ValueError("dloss must be a one-element float32 tensor")
+    dev = hidden.device
+    out = {
+        "loss_mean": torch.empty(1, dtype=torch.float32, device=dev),
+        "loss_rows": torch.empty(max(N, 1), dtype=torch.float32, device=dev)[:N],
+        "n_valid": torch.empty(1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "grad_hidden": torch.empty_like(hidden, memory_format=torch.contiguous_format) if want_grad_hidden else None,
+        "grad_weight": torch.empty_like(weight, memory_format=torch.contiguous_format) if want_grad_weight else None,
+    }
+    gh, gw = out["grad_hidden"], out["grad_weight"]
+    ws = _workspace(dev, ce_linear_workspace_bytes(N, H, V, chunk_rows, hidden.dtype), workspace)
+    rc = _lib.load().ce_linear_fwd_bwd(
+        _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(labels), N, H, V, dt, ignore_index, chunk_rows, _ptr(dloss),
+        _ptr(out["loss_mean"]), _ptr(out["loss_rows"]), _ptr(out["n_valid"]), _ptr(out["status"]), _ptr(gh),
+        H if gh is None else (gh.stride(0) if N > 1 else H), _ptr(gw), H if gw is None else (gw.stride(0) if V > 1 else H),
+        _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(rc, "ce_linear_fwd_bwd")
     return out
 
 

@@ -11,7 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ce_api.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "ce_kernels.h"), os.path.join(ROOT, "include", "ce_mi355x.h")]
+SRCS = [SRC, os.path.join(HERE, "csrc", "ce_linear.hip")]
+DEPS = SRCS + [os.path.join(HERE, "csrc", "ce_kernels.h"), os.path.join(ROOT, "include", "ce_mi355x.h")]
+LIBS = ["-lrocblas"]  # the LM-head entry point's GEMMs
 LIB = os.path.join(HERE, "libce_mi355x.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib_copy.hip")
 CALIB_LIB = os.path.join(HERE, "libce_calib.so")
@@ -37,9 +39,9 @@ def up_to_date() -> bool:
     return all(os.path.getmtime(d) <= t for d in DEPS)
 
 
-def _compile(src: str, out: str, verbose: bool) -> None:
+def _compile(srcs, out: str, verbose: bool, libs=()) -> None:
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp, src]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + list(srcs) + list(libs)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,8 +54,8 @@ def build(force: bool = True, verbose: bool = False) -> str:
     """Compile the library and the counter-calibration copy (always when force=True)."""
     if not force and up_to_date() and os.path.exists(CALIB_LIB):
         return LIB
-    _compile(SRC, LIB, verbose)
-    _compile(CALIB_SRC, CALIB_LIB, verbose)
+    _compile(SRCS, LIB, verbose, LIBS)
+    _compile([CALIB_SRC], CALIB_LIB, verbose)
     return LIB
 
 

@@ -24,7 +24,8 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a device pointer owned by the caller; the
- *     library allocates no memory and keeps no pointer after return.
+ *     library allocates no memory and keeps no pointer after return (the
+ *     LM-head entry point's GEMM library is the one exception, see there).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
  *     stream).  No entry point synchronises the stream or reads device data on
  *     the host; outputs are valid once the stream work completes, and inputs
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 1
+#define CE_ABI_VERSION 2
 
 /* element formats of logits and gradients */
 enum ce_dtype { CE_DTYPE_F32 = 0, CE_DTYPE_BF16 = 1, CE_DTYPE_F16 = 2 };
@@ -100,10 +101,12 @@ int ce_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  * Forward pass.
  *   chunk         vocabulary slab width for the per-chunk log-sum-exp merge
  *                 (lse = M + log sum_c exp(lse_c - M), M = max_c lse_c; PR #79
- *                 "TODO": chunked loss).  0 = no chunking (the whole row is
- *                 reduced at once when it fits on chip; larger rows are chunked
- *                 at 65536 automatically).  The result does not depend on chunk
- *                 beyond rounding.
+ *                 "TODO": chunked loss) of rows too wide to be held on chip
+ *                 (> 131072 bf16/fp16 or > 65536 fp32 elements); 0 = 65536
+ *                 (fp32: 32768).  A row that fits on chip is reduced whole in
+ *                 one pass whatever chunk is: its workgroup merges (max, sum)
+ *                 partials of many lanes, a finer partition of the same merge.
+ *                 The result does not depend on chunk beyond rounding.
  *   loss_mean     out, 1 float: L (NaN when n_valid == 0).
  *   loss_rows     out, n_rows floats: per-row loss (0 for ignored rows).
  *   lse_rows      out or NULL, n_rows doubles: per-row lse (0 for ignored rows).
@@ -152,6 +155,58 @@ int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t 
                        const float* dloss, float* loss_mean, float* loss_rows, double* lse_rows,
                        double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * LM-head projection followed by the cross-entropy above, forward and
+ * backward, token-chunked.  The pages compare the plain kernel with a fused
+ * linear cross-entropy (PyPI page "fms-acceleration-foak 0.7.4", "Running
+ * Liger Kernel Benchmarks"), list fused cross-entropy among the kernels to
+ * come (fms-hf-tuning PR #280, "Notes on FastKernels") and leave a chunked
+ * loss as a to-do (fms-acceleration PR #79, "TODO").  With hidden states
+ * h [n_rows, hidden_size] and the weight W [vocab, hidden_size] of a bias-free
+ * linear layer:
+ *
+ *   logits      = h W^T          (fp32, never stored beyond chunk_rows rows)
+ *   L, loss_rows, n_valid, status  as ce_forward on those logits
+ *   grad_hidden = g W,  grad_weight = g^T h,  g = dloss * dL/dlogits
+ *
+ * Rows are processed chunk_rows at a time (0 = 1024; rounded up to a multiple
+ * of 64, and up so that there are at most 4096 chunks): the chunk's logits by
+ * a library GEMM (rocBLAS: inputs in dtype, fp32 accumulation, fp32 result),
+ * its loss and gradient by the kernels of ce_fwd_bwd_inplace on those fp32
+ * logits (fp64 arithmetic) with the token mean over the whole batch, the
+ * gradient rounded to dtype (bf16 / fp16) for the two backward GEMMs (fp32
+ * accumulation); grad_weight is accumulated in fp32 over the chunks and
+ * rounded once to dtype at the end.
+ *   hidden        n_rows rows of hidden_size elements of dtype, row i at
+ *                 i * ld_hidden (ld_hidden >= hidden_size).
+ *   weight        vocab rows of hidden_size elements, row v at v * ld_weight.
+ *   labels        n_rows int64 class indices in [0, vocab) or ignore_index.
+ *   dloss         device float or NULL (= 1.0): the upstream gradient of L.
+ *   loss_mean, loss_rows, n_valid, status: as ce_forward (loss_rows required).
+ *   grad_hidden   out or NULL (not computed): n_rows rows, stride ld_grad_hidden.
+ *   grad_weight   out or NULL: vocab rows, stride ld_grad_weight (all zeros when
+ *                 n_rows == 0).
+ *   workspace     ce_linear_workspace_bytes(...) bytes, 256-byte aligned,
+ *                 prepared once with ce_workspace_init: the cross-entropy
+ *                 workspace of a chunk, a chunk of fp32 logits and, for
+ *                 bf16/fp16, the chunk's rounded gradient and the fp32
+ *                 grad_weight accumulator (vocab x hidden_size x 4 bytes).
+ * Memory: apart from the workspace, rocBLAS keeps one handle per device for the
+ * process lifetime (with the memory it allocates for itself); calls on one
+ * device are serialised on the host around that handle.
+ * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
+ * dimension of 2^31 or more give CE_ERR_UNSUPPORTED (the GEMMs take 32-bit
+ * sizes); a failed GEMM gives CE_ERR_HIP.
+ */
+size_t ce_linear_workspace_bytes(int64_t n_rows, int64_t hidden_size, int64_t vocab, int64_t chunk_rows,
+                                 int dtype);
+int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight, int64_t ld_weight,
+                      const int64_t* labels, int64_t n_rows, int64_t hidden_size, int64_t vocab, int dtype,
+                      int64_t ignore_index, int64_t chunk_rows, const float* dloss, float* loss_mean,
+                      float* loss_rows, int32_t* n_valid, uint32_t* status, void* grad_hidden,
+                      int64_t ld_grad_hidden, void* grad_weight, int64_t ld_grad_weight, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

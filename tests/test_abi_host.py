@@ -137,3 +137,54 @@ def test_workspace_init_rejects(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def linear(lib, hidden=FAKE, ldh=64, weight=FAKE, ldw=64, labels=FAKE, N=8, H=64, V=100, dtype=1, ignore=-100,
+           chunk=0, dloss=None, loss_mean=FAKE, loss_rows=FAKE, n_valid=FAKE, status=FAKE, gh=FAKE, ldgh=64,
+           gw=FAKE, ldgw=64, ws=FAKE, ws_bytes=1 << 30):
+    return lib.ce_linear_fwd_bwd(VP(hidden), ldh, VP(weight), ldw, VP(labels), N, H, V, dtype, ignore, chunk,
+                                 VP(dloss), VP(loss_mean), VP(loss_rows), VP(n_valid), VP(status), VP(gh), ldgh,
+                                 VP(gw), ldgw, VP(ws), ws_bytes, None)
+
+
+def test_linear_workspace_bytes(lib):
+    b = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_BF16)
+    # one fp32 chunk of logits, its bf16 gradient and the fp32 weight-gradient accumulator
+    assert b >= 1024 * 32000 * 4 + 1024 * 32000 * 2 + 32000 * 4096 * 4
+    f32 = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_F32)
+    assert 1024 * 32000 * 4 <= f32 < b  # fp32: no rounded copy, accumulates in the output
+    assert lib.ce_linear_workspace_bytes(4096, 4096, 32000, 64, 1) < b  # smaller chunks, smaller workspace
+    assert lib.ce_linear_workspace_bytes(-1, 64, 10, 0, 1) == 0
+    assert lib.ce_linear_workspace_bytes(4, 0, 10, 0, 1) == 0
+    assert lib.ce_linear_workspace_bytes(4, 64, 10, -1, 1) == 0
+    assert lib.ce_linear_workspace_bytes(4, 64, 10, 0, 5) == 0
+    assert lib.ce_linear_workspace_bytes(4, 64, 1 << 31, 0, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.CE_ERR_DTYPE),
+    (dict(N=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(H=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(V=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldh=63), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldw=10), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldgh=63), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldgw=1), _lib.CE_ERR_INVALID_ARG),
+    (dict(hidden=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(weight=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(labels=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(loss_rows=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(loss_mean=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(n_valid=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(hidden=FAKE + 1), _lib.CE_ERR_INVALID_ARG),
+    (dict(gw=FAKE + 1), _lib.CE_ERR_INVALID_ARG),
+    (dict(labels=FAKE + 4), _lib.CE_ERR_INVALID_ARG),
+    (dict(chunk=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(ws=0), _lib.CE_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), _lib.CE_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.CE_ERR_WORKSPACE),
+    (dict(V=1 << 31), _lib.CE_ERR_UNSUPPORTED),
+    (dict(ldh=1 << 31), _lib.CE_ERR_UNSUPPORTED),
+])
+def test_linear_rejects(lib, kw, code):
+    assert linear(lib, **kw) == code

@@ -1,0 +1,195 @@
+"""GPU parity of the LM-head + cross-entropy entry point against the float64
+oracle (oracle/linear.py), through the C ABI.
+
+Tolerance, from the arithmetic (u_d: unit roundoff of the storage format,
+2^-8 bf16, 2^-11 fp16, 2^-24 fp32; gamma_K = K 2^-24 for an fp32 sum of K
+exact products):
+  logits   |x~ - x| <= E_i = gamma_H max_v sum_k |h_ik| |W_vk|        (row i)
+  loss     |loss~ - loss| <= 2 E_i + 2^-23 |loss|   (lse and x_y each move by
+           at most E_i; the fp32 loss is rounded once)
+  g        g~ = RN_d(s (p~ - onehot)): |g~ - g| <= u_d |g| + s p (e^{2E} - 1)
+           (fp16: g is scaled by 2^k before rounding, s 2^k in [2^14, 2^15), so
+           elements below fp16's normal range add at most s 2^-39 each)
+  dh       |dh~ - dh| <= (u_d + gamma_V) (|g| |W|) + 2.1 E_i s (p |W|) + u_d |dh| + tiny
+  dW       |dW~ - dW| <= (u_d + gamma_N) (|g|^T |h|) + 2.1 (E s p)^T |h| + u_d |dW| + tiny
+(products of absolute values in float64; "tiny" is the format's smallest
+subnormal).  The bounds are worst cases: the typical error is reported and is
+far below them.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import cross_entropy_loss_amd as ce
+import oracle
+from oracle import linear as lin
+from workloads import to_storage
+
+pytestmark = pytest.mark.gpu
+
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -24}
+TINY = {"bf16": 2.0 ** -133, "f16": 2.0 ** -24, "f32": 2.0 ** -149}
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this machine")
+    ce._lib.load()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def make(seed, N, H, V, dtype, sigma_w=None, ignore_frac=0.1):
+    rng = np.random.default_rng(seed)
+    sigma_w = sigma_w if sigma_w is not None else 2.0 / math.sqrt(H)  # logits of spread ~2
+    h = to_storage(rng.standard_normal((N, H)), dtype)
+    w = to_storage(rng.standard_normal((V, H)) * sigma_w, dtype)
+    y = rng.integers(0, V, N)
+    y[rng.random(N) < ignore_frac] = -100
+    return h, w, y
+
+
+def to_dev(bits, dtype, ld=None):
+    rows, cols = bits.shape
+    ld = ld or cols
+    raw = torch.from_numpy(np.ascontiguousarray(bits.view(np.int32) if dtype == "f32" else bits.view(np.int16)))
+    buf = torch.zeros(rows * ld + 8, dtype=raw.dtype, device="cuda")
+    view = buf[: rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(raw.cuda())
+    return view.view(TORCH[dtype])
+
+
+def host_bits(t, dtype):
+    t = t.detach().contiguous().cpu()
+    return t.view(torch.int32).numpy().view(np.float32) if dtype == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def run(h, w, y, dtype, dloss=1.0, chunk_rows=0, ldh=None, ldw=None, **kw):
+    _say(f"[linear] dtype={dtype} N,H,V={h.shape[0]},{h.shape[1]},{w.shape[0]} chunk_rows={chunk_rows} "
+         f"ldh={ldh} ldw={ldw} dloss={dloss}")
+    hd, wd = to_dev(h, dtype, ldh), to_dev(w, dtype, ldw)
+    yd = torch.from_numpy(np.ascontiguousarray(y)).cuda()
+    dl = torch.tensor([dloss], dtype=torch.float32, device="cuda")
+    out = ce.ce_linear_fwd_bwd(hd, wd, yd, chunk_rows=chunk_rows, dloss=dl, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(out, h, w, y, dtype, dloss=1.0, expect_status=0):
+    ref = lin.linear_cross_entropy(h, w, y, dtype, dloss=dloss)
+    hx, wx = oracle.widen(h, dtype), oracle.widen(w, dtype)
+    N, H = hx.shape
+    V = wx.shape[0]
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert int(out["status"].item()) == expect_status
+    valid = y != -100
+    bad = valid & ((y < 0) | (y >= V))
+    good = valid & ~bad
+    g16 = 2.0 ** -24
+    E = H * g16 * (np.abs(hx) @ np.abs(wx).T).max(axis=1)  # per row
+    lr = out["loss_rows"].cpu().numpy().astype(np.float64)
+    tol = 2 * E + 2.0 ** -23 * np.abs(ref["loss_rows"]) + 1e-30
+    err = np.abs(lr - ref["loss_rows"])
+    assert (err[good] <= tol[good]).all(), f"loss rows: max err/tol {np.max(err[good] / tol[good])}"
+    assert (lr[~valid] == 0).all()
+    assert np.isnan(lr[bad]).all()
+    L = float(out["loss_mean"].item())
+    if ref["n_valid"] == 0 or bad.any():
+        assert math.isnan(L)
+    else:
+        tolL = np.sum(2 * E[valid]) / ref["n_valid"] + 2.0 ** -22 * abs(ref["loss_mean"])
+        assert abs(L - ref["loss_mean"]) <= tolL, (L, ref["loss_mean"], tolL)
+    if bad.any() or ref["n_valid"] == 0:
+        return ref
+    u = U[dtype]
+    g = ref["grad_logits64"]
+    s = ref["scale"]
+    _, p, _, _, _ = lin.forward64(hx, wx, y)
+    sp = np.where(valid[:, None], s * p, 0.0)
+    for name, got_t, want, A, B, K in (
+            ("grad_hidden", out["grad_hidden"], ref["grad_hidden64"], np.abs(g) @ np.abs(wx),
+             (2.1 * E[:, None] * sp) @ np.abs(wx), V),
+            ("grad_weight", out["grad_weight"], ref["grad_weight64"], np.abs(g).T @ np.abs(hx),
+             (2.1 * E[:, None] * sp).T @ np.abs(hx), N)):
+        if got_t is None:
+            continue
+        got = oracle.widen(host_bits(got_t, dtype), dtype)
+        bound = (u + K * g16) * A + B + u * np.abs(want) + TINY[dtype]
+        if dtype == "f16":
+            # g is rounded to fp16 after scaling by 2^k (s 2^k in [2^14, 2^15)): elements below fp16's
+            # normal range keep an absolute error of 2^-25 2^-k <= s 2^-39 each
+            other = wx if name == "grad_hidden" else hx
+            bound = bound + abs(s) * 2.0 ** -39 * np.abs(other).sum(axis=0)[None, :]
+        d = np.abs(got - want)
+        ratio = d / bound
+        assert (d <= bound).all(), f"{name}: {int((d > bound).sum())} beyond the bound, worst ratio {ratio.max():.3f}"
+        nz = np.abs(want) > 0
+        rel = np.linalg.norm((got - want)[nz]) / max(np.linalg.norm(want[nz]), 1e-300)
+        _say(f"  {name}: worst err/bound {ratio.max():.3f}, relative Frobenius error {rel:.2e}")
+    ign = ~valid
+    if out["grad_hidden"] is not None:
+        gh = host_bits(out["grad_hidden"], dtype)
+        assert (oracle.widen(gh[ign], dtype) == 0).all(), "ignored rows of grad_hidden must be 0"
+    return ref
+
+
+CASES = [("bf16", 256, 384, 3000, 0), ("bf16", 300, 256, 5000, 128), ("f16", 200, 320, 4000, 64),
+         ("f32", 130, 192, 2500, 64), ("bf16", 64, 128, 32000, 0), ("bf16", 513, 512, 1000, 256)]
+
+
+@pytest.mark.parametrize("dtype,N,H,V,chunk", CASES, ids=[f"{d}-N{n}-H{h}-V{v}-c{c}" for d, n, h, v, c in CASES])
+def test_linear_parity(dtype, N, H, V, chunk):
+    h, w, y = make(N + H + V, N, H, V, dtype)
+    out = run(h, w, y, dtype, chunk_rows=chunk)
+    check(out, h, w, y, dtype)
+
+
+def test_linear_strided_and_dloss():
+    h, w, y = make(21, 190, 160, 2100, "bf16")
+    out = run(h, w, y, "bf16", dloss=0.37, chunk_rows=64, ldh=168, ldw=163)
+    check(out, h, w, y, "bf16", dloss=0.37)
+
+
+def test_linear_one_gradient_only():
+    h, w, y = make(22, 100, 128, 1500, "bf16")
+    a = run(h, w, y, "bf16", chunk_rows=64, want_grad_weight=False)
+    assert a["grad_weight"] is None
+    check(a, h, w, y, "bf16")
+    b = run(h, w, y, "bf16", chunk_rows=64, want_grad_hidden=False)
+    assert b["grad_hidden"] is None
+    check(b, h, w, y, "bf16")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192, 0])
+def test_linear_chunk_sizes(chunk):
+    # one row per chunk boundary case: ragged last chunk, a single chunk
+    h, w, y = make(23, 320, 128, 3000, "bf16")
+    check(run(h, w, y, "bf16", chunk_rows=chunk), h, w, y, "bf16")
+
+
+def test_linear_no_valid_rows_and_bad_label():
+    h, w, y = make(24, 70, 64, 500, "bf16")
+    out = run(h, w, np.full(70, -100), "bf16", chunk_rows=64)
+    assert int(out["n_valid"].item()) == 0 and math.isnan(float(out["loss_mean"].item()))
+    assert (oracle.widen(host_bits(out["grad_hidden"], "bf16"), "bf16") == 0).all()
+    assert (oracle.widen(host_bits(out["grad_weight"], "bf16"), "bf16") == 0).all()
+    y2 = y.copy()
+    y2[5] = 500
+    out = run(h, w, y2, "bf16", chunk_rows=64)
+    check(out, h, w, y2, "bf16", expect_status=ce.CE_STATUS_LABEL_RANGE)
+
+
+def test_linear_deterministic():
+    h, w, y = make(25, 200, 256, 2000, "bf16")
+    a = run(h, w, y, "bf16", chunk_rows=64)
+    b = run(h, w, y, "bf16", chunk_rows=64)
+    for k in ("loss_rows", "grad_hidden", "grad_weight"):
+        assert torch.equal(a[k], b[k]), k

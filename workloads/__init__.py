@@ -206,3 +206,62 @@ def make(w: Workload, threads: int | None = None):
     """(logits [N, V] storage array, Plan) for the whole workload."""
     p = plan(w)
     return logits(w, None, p, threads), p
+
+
+# ---------------------------------------------------------------------------
+# LM-head projection inputs: hidden states h [N, H] and the weight W [V, H] of
+# a bias-free linear layer (the Mistral-7B head: hidden 4096, vocabulary
+# 32000).  Hidden values are standard normal; weights are normal with
+# standard deviation sigma_w / sqrt(H), so the logits h W^T have standard
+# deviation ~sigma_w, like the cross-entropy workloads above.
+# Recipe: hidden rows in blocks of BLOCK_ROWS drawn from (seed, 3, b), weight
+# rows from (seed, 4, b), labels and ignored rows from (seed, 2); every value
+# is rounded float64 -> float32 -> storage format (nearest-even).
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    seed: int
+    N: int
+    H: int
+    V: int
+    dtype: str
+    sigma_w: float = 2.0
+    ignore_frac: float = 0.05
+    dloss: float = 1.0
+    chunk_rows: int = 1024
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+LINEAR_WORKLOADS = {
+    1: LinearWorkload("mistral7b-lmhead-b4s1024-bf16", 6, 4096, 4096, 32000, "bf16"),
+}
+
+
+def _normal_rows(seed: int, stream: int, rows: int, cols: int, scale: float, dtype: str, threads: int):
+    out = np.empty((rows, cols), storage_dtype(dtype))
+
+    def work(b):
+        r0 = b * BLOCK_ROWS
+        n = min(BLOCK_ROWS, rows - r0)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((seed, stream, b))))
+        out[r0:r0 + n] = to_storage(rng.standard_normal((n, cols)) * scale, dtype)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range((rows + BLOCK_ROWS - 1) // BLOCK_ROWS)))
+    return out
+
+
+def linear_inputs(lw: LinearWorkload, threads: int | None = None):
+    """(hidden [N, H], weight [V, H], labels [N]) storage arrays."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    h = _normal_rows(lw.seed, 3, lw.N, lw.H, 1.0, lw.dtype, threads)
+    w = _normal_rows(lw.seed, 4, lw.V, lw.H, lw.sigma_w / np.sqrt(lw.H), lw.dtype, threads)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((lw.seed, 2))))
+    y = rng.integers(0, lw.V, lw.N)
+    ign = rng.choice(lw.N, int(round(lw.ignore_frac * lw.N)), replace=False)
+    y[ign] = IGNORE_INDEX
+    return h, w, y
