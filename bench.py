@@ -126,6 +126,45 @@ def _db_rows(path, sql):
         con.close()
 
 
+def profile_summary_linear(d: str, workload: int) -> None:
+    """Kernel-trace summary of the LM-head path (bench.py --op linear) ->
+    profiles/ce_linear_<workload>.txt: per kernel the time per call, and for
+    the GEMMs their rate over 2 N H V flops each."""
+    import glob
+    import workloads as wl
+    lw = wl.LINEAR_WORKLOADS[workload if workload in wl.LINEAR_WORKLOADS else 1]
+    trace = (glob.glob(os.path.join(d, "**", "trace_results.db"), recursive=True) or [None])[0]
+    if not trace:
+        raise SystemExit(f"no trace_results.db under {d}")
+    calls = _db_rows(trace, "select count(*) from kernels where name like '%lin_prep_kernel%'")[0][0]
+    rows = _db_rows(trace, "select name, count(*), sum(duration), avg(duration) from kernels "
+                           "group by name order by sum(duration) desc")
+    flops_per_gemm = 2.0 * lw.N * lw.H * lw.V
+    lines = [f"# rocprofv3 summary: LM-head projection + cross-entropy (ce_linear_fwd_bwd), workload {lw.name}",
+             f"# N={lw.N} H={lw.H} V={lw.V} dtype={lw.dtype} chunk_rows={lw.chunk_rows or 'default'}",
+             "# commands (from the repository root):",
+             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
+             f"python bench.py --op linear --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+             f"#   python bench.py --op linear --profile-summary D --workload {workload}", "",
+             f"{calls} calls traced; per call:",
+             f"  {'kernel':72s} {'launches':>8s} {'ms/call':>9s} {'TFLOP/s':>8s}"]
+    total = 0.0
+    for name, n, s, a in rows:
+        if name.startswith(("void at::native", "__amd_rocclr", "cek::ws_fill")):
+            continue  # the benchmark's own flush / copies, the workspace fill
+        per_call = s / calls / 1e6
+        total += per_call
+        rate = ""
+        if name.startswith("Cijk_"):
+            rate = f"{flops_per_gemm / (per_call * 1e-3) / 1e12:8.0f}"
+        lines.append(f"  {name[:72]:72s} {n // calls:8d} {per_call:9.3f} {rate:>8s}")
+    lines.append(f"  {'total':72s} {'':8s} {total:9.3f} {3 * flops_per_gemm / (total * 1e-3) / 1e12:8.0f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"ce_linear_{lw.name}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def profile_summary(d: str, workload: int) -> None:
     """Reads rocprofv3 databases (trace_results.db, fetch_results.db,
     write_results.db under d) and writes profiles/<kernel>_<workload>.txt and
@@ -213,6 +252,9 @@ def bench_linear(args) -> None:
     import cross_entropy_loss_amd as ce
     import workloads as wl
     lw = wl.LINEAR_WORKLOADS[args.workload if args.workload in wl.LINEAR_WORKLOADS else 1]
+    if args.chunk_rows is not None:
+        import dataclasses
+        lw = dataclasses.replace(lw, chunk_rows=args.chunk_rows)
     h, w, y = wl.linear_inputs(lw)
     dev = torch.device("cuda:0")
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[lw.dtype]
@@ -286,9 +328,13 @@ def main():
     ap.add_argument("--profile-summary", metavar="DIR")
     ap.add_argument("--op", choices=["ce", "linear"], default="ce",
                     help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy")
+    ap.add_argument("--chunk-rows", type=int, default=None, help="--op linear: rows per chunk")
     args = ap.parse_args()
     if args.profile_summary:
-        profile_summary(args.profile_summary, args.workload)
+        if args.op == "linear":
+            profile_summary_linear(args.profile_summary, args.workload)
+        else:
+            profile_summary(args.profile_summary, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",

@@ -36,11 +36,16 @@
 
 #include <mutex>
 
+#include "ce_internal.h"
 #include "ce_mi355x.h"
 
 namespace {
 
-constexpr int64_t kDefaultChunkRows = 1024;
+// 4096 rows: the chunk's fp32 logits and rounded gradient take 4096 V 6
+// bytes (786 MB at V = 32000), and the GEMMs run at their larger-shape
+// rate (4096 x 4096 x 32000 bf16: 3.7 ms per call against 5.5 ms with
+// 1024-row chunks).
+constexpr int64_t kDefaultChunkRows = 4096;
 constexpr int64_t kMaxChunks = 4096;  // per-chunk counts live in LDS
 constexpr int kNT = 1024;
 
@@ -147,14 +152,27 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
 }
 
 // fp32 * scale (a power of two, or NULL = 1) -> storage format, nearest-even,
-// one workgroup per row.
+// one workgroup per row: 16-byte loads and 8-byte stores where the row's
+// alignment allows (a per-row choice), single elements otherwise.
 template <typename T>
 __global__ __launch_bounds__(256) void lin_cast_kernel(const float* src, int64_t ld_src, int64_t cols, T* dst,
                                                        int64_t ld_dst, const float* scale) {
   const float* s = src + (int64_t)blockIdx.x * ld_src;
   T* d = dst + (int64_t)blockIdx.x * ld_dst;
   const float f = scale ? scale[0] : 1.0f;
-  for (int64_t j = threadIdx.x; j < cols; j += 256) d[j] = (T)(s[j] * f);
+  int64_t j0 = 0;
+  if ((uintptr_t)s % 16 == 0 && (uintptr_t)d % 8 == 0) {
+    const int64_t n4 = cols / 4;
+    for (int64_t q = threadIdx.x; q < n4; q += 256) {
+      const float4 x = ((const float4*)s)[q];
+      const T o[4] = {(T)(x.x * f), (T)(x.y * f), (T)(x.z * f), (T)(x.w * f)};
+      uint2 w;
+      __builtin_memcpy(&w, o, sizeof(w));
+      ((uint2*)d)[q] = w;
+    }
+    j0 = n4 * 4;
+  }
+  for (int64_t j = j0 + threadIdx.x; j < cols; j += 256) d[j] = (T)(s[j] * f);
 }
 
 __global__ __launch_bounds__(256) void lin_zero_kernel(uint16_t* dst, int64_t ld, int64_t cols, int esz) {
@@ -327,23 +345,34 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
     rc = gemm(bh, rocblas_operation_transpose, rocblas_operation_none, V, Tc, H, one, weight, dt, ld_weight, hc, dt,
               ld_hidden, zero, logits, rocblas_datatype_f32_r, V);
     if (rc != CE_OK) break;
-    // 2. the chunk's losses and g (in place over the fp32 logits)
-    rc = ce_fwd_bwd_inplace(logits, V, labels + r0, Tc, V, CE_DTYPE_F32, ignore_index, 0, dl_chunk + c,
-                            chunk_loss + c, loss_rows + r0, nullptr, nullptr, chunk_n + c, chunk_status + c,
-                            ws + L.ce_ws, L.ce_ws_bytes, st);
-    if (rc != CE_OK) break;
-    if (grad_hidden == nullptr && grad_weight == nullptr) continue;
-    // 3. g in the input format for the GEMMs
-    if (dtype == CE_DTYPE_BF16)
-      hipLaunchKernelGGL(lin_cast_kernel<__bf16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
-                         (__bf16*)g_lo, V, (const float*)nullptr);
-    else if (dtype == CE_DTYPE_F16)
-      hipLaunchKernelGGL(lin_cast_kernel<_Float16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
-                         (_Float16*)g_lo, V, (const float*)nullptr);
-    if (hipGetLastError() != hipSuccess) {
-      rc = CE_ERR_HIP;
-      break;
+    // 2-3. the chunk's losses and g: for bf16 / fp16 one kernel reads the fp32
+    // logits and writes g in the input format for the GEMMs; otherwise (fp32,
+    // or rows it does not serve) g is written over the fp32 logits and cast
+    bool fused = false;
+    if (dtype != CE_DTYPE_F32) {
+      rc = ce_lin_chunk_f32_to16(logits, V, labels + r0, Tc, V, dtype, ignore_index, dl_chunk + c, chunk_loss + c,
+                                 loss_rows + r0, chunk_n + c, chunk_status + c, g_lo, V, ws + L.ce_ws,
+                                 L.ce_ws_bytes, st);
+      if (rc == CE_OK) fused = true;
+      else if (rc != CE_ERR_UNSUPPORTED) break;
     }
+    if (!fused) {
+      rc = ce_fwd_bwd_inplace(logits, V, labels + r0, Tc, V, CE_DTYPE_F32, ignore_index, 0, dl_chunk + c,
+                              chunk_loss + c, loss_rows + r0, nullptr, nullptr, chunk_n + c, chunk_status + c,
+                              ws + L.ce_ws, L.ce_ws_bytes, st);
+      if (rc != CE_OK) break;
+      if (dtype == CE_DTYPE_BF16)
+        hipLaunchKernelGGL(lin_cast_kernel<__bf16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
+                           (__bf16*)g_lo, V, (const float*)nullptr);
+      else if (dtype == CE_DTYPE_F16)
+        hipLaunchKernelGGL(lin_cast_kernel<_Float16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
+                           (_Float16*)g_lo, V, (const float*)nullptr);
+      if (hipGetLastError() != hipSuccess) {
+        rc = CE_ERR_HIP;
+        break;
+      }
+    }
+    if (grad_hidden == nullptr && grad_weight == nullptr) continue;
     // 4. dh_c [Tc x H] = g W  (column-major: H x Tc = (H x V)(V x Tc))
     if (grad_hidden) {
       rc = gemm(bh, rocblas_operation_none, rocblas_operation_none, H, Tc, V, down, weight, dt, ld_weight, g_lo, dt,

@@ -141,8 +141,11 @@ def check(out, h, w, y, dtype, dloss=1.0, expect_status=0):
     return ref
 
 
+# vocab a multiple of 4 takes the one-kernel fp32 -> bf16/fp16 gradient step; 3001 / 2999 the in-place
+# fp32 step followed by a cast
 CASES = [("bf16", 256, 384, 3000, 0), ("bf16", 300, 256, 5000, 128), ("f16", 200, 320, 4000, 64),
-         ("f32", 130, 192, 2500, 64), ("bf16", 64, 128, 32000, 0), ("bf16", 513, 512, 1000, 256)]
+         ("f32", 130, 192, 2500, 64), ("bf16", 64, 128, 32000, 0), ("bf16", 513, 512, 1000, 256),
+         ("bf16", 150, 192, 3001, 64), ("f16", 140, 160, 2999, 64)]
 
 
 @pytest.mark.parametrize("dtype,N,H,V,chunk", CASES, ids=[f"{d}-N{n}-H{h}-V{v}-c{c}" for d, n, h, v, c in CASES])

@@ -229,7 +229,7 @@ class LinearWorkload:
     sigma_w: float = 2.0
     ignore_frac: float = 0.05
     dloss: float = 1.0
-    chunk_rows: int = 1024
+    chunk_rows: int = 0  # 0: the library's default (4096 rows)
 
     @property
     def elem_bytes(self) -> int:
