@@ -22,7 +22,8 @@ from ._lib import (CE_STATUS_LABEL_RANGE, CE_STATUS_SYNC_TIMEOUT, CeError)  # no
 __all__ = [
     "ce_workspace_bytes", "ce_workspace_init", "Workspace", "ce_forward", "ce_backward",
     "ce_fwd_bwd_inplace", "cross_entropy", "FastCrossEntropyLoss", "CeError",
-    "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
+    "ce_linear_workspace_bytes", "ce_linear_fwd_bwd", "ce_rmsnorm_workspace_bytes", "ce_rmsnorm_forward",
+    "ce_rmsnorm_backward", "rms_norm", "FastRMSNorm",
 ]
 
 _DTYPES = {torch.float32: _lib.CE_DTYPE_F32, torch.bfloat16: _lib.CE_DTYPE_BF16,
@@ -232,6 +233,98 @@ def ce_linear_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
         _ptr(ws), ws.numel(), _stream(dev))
     _lib.check(rc, "ce_linear_fwd_bwd")
     return out
+
+
+_norm_ws: dict = {}
+
+
+def ce_rmsnorm_workspace_bytes(n_rows: int, hidden: int, dtype: torch.dtype) -> int:
+    n = _lib.load().ce_rmsnorm_workspace_bytes(n_rows, hidden, _DTYPES[dtype])
+    if n == 0:
+        raise ValueError("no RMSNorm workspace size for these arguments")
+    return int(n)
+
+
+def _norm_weight(weight: torch.Tensor, x: torch.Tensor):
+    if weight.dim() != 1 or weight.numel() != x.shape[1] or weight.dtype != x.dtype or weight.device != x.device \
+            or (weight.numel() > 1 and weight.stride(0) != 1):
+        raise ValueError("weight must be a contiguous [hidden] tensor of x's dtype and device")
+
+
+def ce_rmsnorm_forward(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6) -> tuple:
+    """RMS layer normalisation of the rows of x [rows, hidden]: (y, rstd)."""
+    N, H, ldx = _matrix(x, "x")
+    _norm_weight(weight, x)
+    y = torch.empty((N, H), dtype=x.dtype, device=x.device)
+    rstd = torch.empty(max(N, 1), dtype=torch.float32, device=x.device)[:N]
+    rc = _lib.load().ce_rmsnorm_forward(_ptr(x), ldx, _ptr(weight), N, H, _dtype_code(x), eps, _ptr(y), H,
+                                        _ptr(rstd), _stream(x.device))
+    _lib.check(rc, "ce_rmsnorm_forward")
+    return y, rstd
+
+
+def ce_rmsnorm_backward(dy: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, rstd: torch.Tensor,
+                        inplace: bool = False, workspace: torch.Tensor | None = None) -> tuple:
+    """Gradients (dx, dweight) of RMSNorm for the upstream dy; with inplace,
+    dx is written over dy."""
+    N, H, ldx = _matrix(x, "x")
+    N2, H2, lddy = _matrix(dy, "dy")
+    if (N2, H2) != (N, H) or dy.dtype != x.dtype or dy.device != x.device:
+        raise ValueError("dy must match x in shape, dtype and device")
+    _norm_weight(weight, x)
+    if rstd.dtype != torch.float32 or rstd.numel() != N or (N > 1 and rstd.stride(0) != 1) or rstd.device != x.device:
+        raise ValueError("rstd must be a contiguous float32 [rows] tensor on x's device")
+    dx = dy if inplace else torch.empty((N, H), dtype=x.dtype, device=x.device)
+    lddx = lddy if inplace else H
+    dw = torch.empty(H, dtype=x.dtype, device=x.device)
+    # its own scratch: the cross-entropy workspaces carry state from call to call
+    nbytes = ce_rmsnorm_workspace_bytes(N, H, x.dtype)
+    if workspace is None:
+        key = (x.device, torch.cuda.current_stream(x.device).cuda_stream)
+        ws = _norm_ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = _norm_ws[key] = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    else:
+        ws = workspace
+        if ws.dtype != torch.uint8 or ws.numel() < nbytes or not ws.is_cuda:
+            raise ValueError(f"workspace must be a uint8 GPU tensor of at least {nbytes} bytes")
+    rc = _lib.load().ce_rmsnorm_backward(_ptr(dy), lddy, _ptr(x), ldx, _ptr(weight), _ptr(rstd), N, H,
+                                         _dtype_code(x), _ptr(dx), lddx, _ptr(dw), _ptr(ws), ws.numel(),
+                                         _stream(x.device))
+    _lib.check(rc, "ce_rmsnorm_backward")
+    return dx, dw
+
+
+class _RMSNorm(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, weight, eps):
+        y, rstd = ce_rmsnorm_forward(x, weight, eps)
+        ctx.save_for_backward(x, weight, rstd)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, weight, rstd = ctx.saved_tensors
+        dx, dw = ce_rmsnorm_backward(dy.contiguous(), x, weight, rstd)
+        return dx, dw, None
+
+
+def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """RMSNorm over the last dimension with autograd (x [..., hidden])."""
+    H = x.shape[-1]
+    return _RMSNorm.apply(x.reshape(-1, H), weight, eps).reshape(x.shape)
+
+
+class FastRMSNorm(torch.nn.Module):
+    """RMSNorm layer (weight initialised to ones) on the library's kernels."""
+
+    def __init__(self, hidden: int, eps: float = 1e-6, dtype: torch.dtype = torch.bfloat16, device=None):
+        super().__init__()
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+        self.eps = eps
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return rms_norm(x, self.weight, self.eps)
 
 
 class _CrossEntropy(torch.autograd.Function):

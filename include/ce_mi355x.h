@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 2
+#define CE_ABI_VERSION 3
 
 /* element formats of logits and gradients */
 enum ce_dtype { CE_DTYPE_F32 = 0, CE_DTYPE_BF16 = 1, CE_DTYPE_F16 = 2 };
@@ -207,6 +207,46 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
                       float* loss_rows, int32_t* n_valid, uint32_t* status, void* grad_hidden,
                       int64_t ld_grad_hidden, void* grad_weight, int64_t ld_grad_weight, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * RMS layer normalisation, forward and backward.  The pages list "Fast RMS
+ * LayerNorm" among the package's kernels (PyPI page "fms-acceleration-foak
+ * 0.7.4", kernel list) and patch it in for a model's RMSNorm class (same page,
+ * the model-patcher rule that replaces GraniteRMSNorm's forward;
+ * fms-hf-tuning PR #280, "Notes on FastKernels").  Per row x[0..hidden):
+ *
+ *   rstd = 1 / sqrt(mean_j x_j^2 + eps),   y_j = w_j x_j rstd
+ *   dx_j = rstd (w_j dy_j - x^_j mean_k(x^_k w_k dy_k)),   x^ = x rstd
+ *   dw_j = sum over rows of dy_j x^_j
+ *
+ * bf16 / fp16 compute in fp32 and round once; fp32 computes y and dx in fp64.
+ * x, y, dy, dx: n_rows rows of hidden elements of dtype, row i at i * ld_*;
+ * every row pointer 16-byte aligned (pointers and ld * element size multiples
+ * of 16) and hidden a multiple of 8 (16-bit) or 4 (fp32), else
+ * CE_ERR_UNSUPPORTED.  weight, dweight: hidden elements of dtype.  rstd:
+ * n_rows floats, written by the forward and read by the backward.
+ * Forward: hidden up to 16384 (16-bit) / 8192 (fp32); eps >= 0; y may be x
+ * itself (same stride: each row is read whole before it is written).  The
+ * 16-bit sum of squares runs in fp32 and is redone in fp64 when it overflows
+ * or falls below 2^-100; with eps = 0, a row whose root mean square is below
+ * 2^-128 gives rstd = inf.
+ * Backward: hidden up to 4096 (16-bit) / 2048 (fp32); dx may be dy itself
+ * (same stride); dweight is summed over the rows in fixed order
+ * (deterministic) through a workspace of ce_rmsnorm_workspace_bytes() bytes
+ * (256-byte aligned, no preparation needed, contents overwritten: not a
+ * cross-entropy workspace that is still in use); dweight is all zeros when
+ * n_rows == 0.  Errors: CE_ERR_DTYPE, CE_ERR_INVALID_ARG (negative sizes,
+ * ld < hidden, NULL pointers, eps < 0 or NaN, aliasing with another stride,
+ * dweight misaligned for dtype), CE_ERR_UNSUPPORTED (shape or alignment not
+ * served), CE_ERR_WORKSPACE, CE_ERR_HIP (launch failure); nothing is written
+ * on an error return.
+ */
+size_t ce_rmsnorm_workspace_bytes(int64_t n_rows, int64_t hidden, int dtype);
+int ce_rmsnorm_forward(const void* x, int64_t ld_x, const void* weight, int64_t n_rows, int64_t hidden, int dtype,
+                       float eps, void* y, int64_t ld_y, float* rstd, void* stream);
+int ce_rmsnorm_backward(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* weight,
+                        const float* rstd, int64_t n_rows, int64_t hidden, int dtype, void* dx, int64_t ld_dx,
+                        void* dweight, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -188,3 +188,81 @@ def test_linear_workspace_bytes(lib):
 ])
 def test_linear_rejects(lib, kw, code):
     assert linear(lib, **kw) == code
+
+
+def rms_fwd(lib, x=FAKE, ldx=64, w=FAKE, N=8, H=64, dtype=1, eps=1e-6, y=FAKE + 4096, ldy=64, rstd=FAKE):
+    return lib.ce_rmsnorm_forward(VP(x), ldx, VP(w), N, H, dtype, eps, VP(y), ldy, VP(rstd), None)
+
+
+def rms_bwd(lib, dy=FAKE, lddy=64, x=FAKE + 4096, ldx=64, w=FAKE, rstd=FAKE, N=8, H=64, dtype=1, dx=FAKE + 8192,
+            lddx=64, dw=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.ce_rmsnorm_backward(VP(dy), lddy, VP(x), ldx, VP(w), VP(rstd), N, H, dtype, VP(dx), lddx, VP(dw),
+                                   VP(ws), ws_bytes, None)
+
+
+def test_rmsnorm_workspace_bytes(lib):
+    b = lib.ce_rmsnorm_workspace_bytes(4096, 4096, _lib.CE_DTYPE_BF16)
+    assert b >= 4096 * 4 and b % 256 == 0  # at least one fp32 partial row of dweight
+    assert b <= 1024 * 4096 * 4            # a bounded number of partial rows, not one per token
+    assert lib.ce_rmsnorm_workspace_bytes(1, 8, 1) >= 8 * 4
+    assert lib.ce_rmsnorm_workspace_bytes(0, 64, 1) >= 64 * 4  # the zero-row backward still reduces
+    assert lib.ce_rmsnorm_workspace_bytes(-1, 64, 1) == 0
+    assert lib.ce_rmsnorm_workspace_bytes(4, 0, 1) == 0
+    assert lib.ce_rmsnorm_workspace_bytes(4, 60, 1) == 0   # not a multiple of 8 (16-bit)
+    assert lib.ce_rmsnorm_workspace_bytes(4, 60, 0) > 0    # fp32: multiple of 4
+    assert lib.ce_rmsnorm_workspace_bytes(4, 64, 5) == 0
+
+
+def test_rmsnorm_zero_rows_forward_is_a_no_op(lib):
+    # nothing is launched for an empty batch, so the fake pointers are never touched
+    assert rms_fwd(lib, N=0) == _lib.CE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.CE_ERR_DTYPE),
+    (dict(N=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(H=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldy=8), _lib.CE_ERR_INVALID_ARG),
+    (dict(eps=-1e-6), _lib.CE_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _lib.CE_ERR_INVALID_ARG),
+    (dict(x=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(w=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(y=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(rstd=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(y=FAKE, ldy=72), _lib.CE_ERR_INVALID_ARG),   # in place with another stride
+    (dict(H=60, ldx=64, ldy=64), _lib.CE_ERR_UNSUPPORTED),
+    (dict(H=16392, ldx=16392, ldy=16392), _lib.CE_ERR_UNSUPPORTED),
+    (dict(dtype=0, H=8196, ldx=8196, ldy=8196), _lib.CE_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 2), _lib.CE_ERR_UNSUPPORTED),
+    (dict(ldx=68), _lib.CE_ERR_UNSUPPORTED),            # 136-byte rows: not 16-byte aligned
+])
+def test_rmsnorm_forward_rejects(lib, kw, code):
+    assert rms_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.CE_ERR_DTYPE),
+    (dict(N=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(H=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(lddy=63), _lib.CE_ERR_INVALID_ARG),
+    (dict(ldx=1), _lib.CE_ERR_INVALID_ARG),
+    (dict(lddx=32), _lib.CE_ERR_INVALID_ARG),
+    (dict(dw=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(w=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(dy=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(x=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(rstd=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(dx=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(dw=FAKE + 1), _lib.CE_ERR_INVALID_ARG),
+    (dict(dx=FAKE, lddx=72), _lib.CE_ERR_INVALID_ARG),  # in place with another stride
+    (dict(H=4104, lddy=4104, ldx=4104, lddx=4104), _lib.CE_ERR_UNSUPPORTED),
+    (dict(dtype=0, H=2052, lddy=2052, ldx=2052, lddx=2052), _lib.CE_ERR_UNSUPPORTED),
+    (dict(H=12, lddy=12, ldx=12, lddx=12), _lib.CE_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 8), _lib.CE_ERR_UNSUPPORTED),
+    (dict(ws=0), _lib.CE_ERR_WORKSPACE),
+    (dict(ws_bytes=100), _lib.CE_ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), _lib.CE_ERR_WORKSPACE),
+])
+def test_rmsnorm_backward_rejects(lib, kw, code):
+    assert rms_bwd(lib, **kw) == code
