@@ -42,12 +42,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 BASELINE_METRIC = "CE fwd+bwd tokens/s and HBM GB/s (% of peak), N=4096 V=32000 bf16"
-KERNEL_SOURCES = ["cross_entropy_loss_amd/csrc/ce_kernels.h", "cross_entropy_loss_amd/csrc/ce_api.hip"]
+KERNEL_SOURCES = ["cross_entropy_loss_amd/csrc/ce_kernels.h", "cross_entropy_loss_amd/csrc/ce_buffer.h",
+                  "cross_entropy_loss_amd/csrc/ce_api.hip"]
 
 
-def kernel_sha() -> str:
+NORM_SOURCES = ["cross_entropy_loss_amd/csrc/rmsnorm.hip", "cross_entropy_loss_amd/csrc/ce_buffer.h"]
+
+
+def kernel_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -62,7 +66,7 @@ def algorithmic_bytes(w, labels) -> int:
     return (2 * n_valid + n_ign) * w.V * w.elem_bytes + w.N * (8 + 4 + 8 + 8)
 
 
-def measured_traffic(name: str):
+def measured_traffic(name: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"{name}.counters.json")
@@ -70,7 +74,7 @@ def measured_traffic(name: str):
         return None
     with open(p) as f:
         c = json.load(f)
-    if c.get("kernel_sha") != kernel_sha():
+    if c.get("kernel_sha") != kernel_sha(sources):
         return None
     return c.get("traffic_bytes")
 
@@ -132,7 +136,8 @@ def profile_summary_linear(d: str, workload: int) -> None:
     the GEMMs their rate over 2 N H V flops each."""
     import glob
     import workloads as wl
-    lw = wl.LINEAR_WORKLOADS[workload if workload in wl.LINEAR_WORKLOADS else 1]
+    workload = workload if workload in wl.LINEAR_WORKLOADS else 1
+    lw = wl.LINEAR_WORKLOADS[workload]
     trace = (glob.glob(os.path.join(d, "**", "trace_results.db"), recursive=True) or [None])[0]
     if not trace:
         raise SystemExit(f"no trace_results.db under {d}")
@@ -317,6 +322,209 @@ def bench_linear(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+def norm_bytes(nw) -> dict:
+    """Algorithmic HBM bytes of the two RMSNorm calls: the forward reads x and
+    the weight and writes y and rstd; the backward reads dy, x, the weight and
+    rstd and writes dx and dweight (the workgroups' partial sums of dweight are
+    the implementation's, not the algorithm's)."""
+    e, N, H = nw.elem_bytes, nw.N, nw.H
+    return {"forward": 2 * N * H * e + H * e + 4 * N, "backward": 3 * N * H * e + 2 * H * e + 4 * N}
+
+
+NORM_KERNELS = ("rms_fwd", "rms_bwd", "rms_dw_reduce")
+
+
+def profile_summary_norm(d: str, workload: int) -> None:
+    """rocprofv3 databases of bench.py --op rmsnorm runs -> profiles/rmsnorm_<workload>.txt
+    and the counters JSON that bench.py reads for roofline.traffic (the
+    backward call: rms_bwd* + rms_dw_reduce)."""
+    import glob
+    import workloads as wl
+    workload = workload if workload in wl.NORM_WORKLOADS else 1
+    nw = wl.NORM_WORKLOADS[workload]
+    find = lambda stem: (glob.glob(os.path.join(d, "**", f"{stem}_results.db"), recursive=True) or [None])[0]
+    trace, fetch, write = find("trace"), find("fetch"), find("write")
+    ab = norm_bytes(nw)
+    sha = kernel_sha(NORM_SOURCES)
+    lines = [f"# rocprofv3 summary: RMSNorm forward and backward, workload {nw.name}",
+             f"# N={nw.N} H={nw.H} dtype={nw.dtype} eps={nw.eps}; kernel sources sha {sha}",
+             "# commands (from the repository root):",
+             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
+             f"python bench.py --op rmsnorm --workload {workload} --steps 10 --no-cpu-baseline",
+             "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- "
+             f"python bench.py --op rmsnorm --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
+             "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- "
+             f"python bench.py --op rmsnorm --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
+             f"#   python bench.py --op rmsnorm --profile-summary D --workload {workload}", ""]
+    rec = {"kernel_sha": sha, "workload": nw.name, "algorithmic_bytes": ab}
+    med = {}
+    if trace:
+        rows = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
+                               "group by name order by sum(duration) desc")
+        lines.append("kernel-trace (durations in us; the first calls of a run are cold):")
+        lines.append(f"  {'kernel':70s} {'calls':>5s} {'avg':>9s} {'median':>9s} {'min':>9s} {'max':>9s}")
+        for name, n, avg, mn, mx in rows:
+            durs = sorted(r[0] for r in _db_rows(trace, "select duration from kernels where name = '%s'"
+                                                       % name.replace("'", "''")))
+            m = durs[len(durs) // 2] / 1e3
+            lines.append(f"  {name[:70]:70s} {n:5d} {avg / 1e3:9.2f} {m:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}")
+            for k in NORM_KERNELS:
+                if k in name:
+                    med[k] = m
+        lines.append("")
+    nbytes = nw.N * nw.H * nw.elem_bytes
+    for tag, db, counter in (("read", fetch, "FETCH_SIZE"), ("write", write, "WRITE_SIZE")):
+        if not db:
+            continue
+        rows = _db_rows(db, f"select kernel_name, avg(value), count(*) from counters_collection "
+                            f"where counter_name = '{counter}' group by kernel_name")
+        calib = [r for r in rows if "calib_copy" in r[0]]
+        lines.append(f"{counter} (KiB per dispatch, as reported):")
+        for name, val, n in rows:
+            lines.append(f"  {name[:70]:70s} {val:14.1f}  ({n} dispatches)")
+        if calib:
+            factor = (nbytes / 1024.0) / calib[0][1]
+            rec[f"{tag}_factor"] = factor
+            for part, keys in (("forward", ("rms_fwd",)), ("backward", ("rms_bwd", "rms_dw_reduce"))):
+                kib = sum(r[1] for r in rows if any(k in r[0] for k in keys))
+                rec[f"{part}_{tag}_bytes"] = kib * 1024.0 * factor
+                lines.append(f"  {part}: {kib:.1f} KiB x {factor:.4f} = {kib * 1024 * factor / 1e6:.2f} MB")
+            lines.append(f"  calibration: copy of {nbytes} B reads as {calib[0][1]:.1f} KiB -> factor {factor:.4f}")
+        lines.append("")
+    for part in ("forward", "backward"):
+        if f"{part}_read_bytes" in rec and f"{part}_write_bytes" in rec:
+            t = rec[f"{part}_read_bytes"] + rec[f"{part}_write_bytes"]
+            rec[f"{part}_traffic_bytes"] = t
+            lines.append(f"HBM traffic, {part} call: {t / 1e6:.2f} MB (algorithmic {ab[part] / 1e6:.2f} MB, "
+                         f"ratio {t / ab[part]:.3f})")
+    if "rms_bwd" in med:
+        bw_us = med["rms_bwd"] + med.get("rms_dw_reduce", 0.0)
+        rec["backward_us"] = bw_us
+        lines.append(f"backward call: rms_bwd {med['rms_bwd']:.2f} + rms_dw_reduce {med.get('rms_dw_reduce', 0):.2f} us"
+                     f" -> {ab['backward'] / (bw_us * 1e-6) / 1e9:.0f} GB/s algorithmic "
+                     f"({ab['backward'] / (bw_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f} GB/s)")
+    if "rms_fwd" in med:
+        rec["forward_us"] = med["rms_fwd"]
+        lines.append(f"forward call: rms_fwd {med['rms_fwd']:.2f} us -> "
+                     f"{ab['forward'] / (med['rms_fwd'] * 1e-6) / 1e9:.0f} GB/s algorithmic")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"rmsnorm_{nw.name}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if fetch or write:
+        with open(os.path.join(ROOT, "profiles", f"rmsnorm_{nw.name}.counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+def _calib_copy_gbs(src, dst, nbytes, flush, stream, reps):
+    """Read + write rate of a plain copy of nbytes with the kernels' 16-byte
+    nontemporal loads and stores (median of the warm repetitions)."""
+    import ctypes
+    import torch
+    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
+    calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    cms = []
+    for i in range(reps):
+        flush.fill_(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = calib.ce_calib_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                 ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc:
+            raise SystemExit(f"calibration copy failed: {rc}")
+        torch.cuda.synchronize()
+        cms.append(e0.elapsed_time(e1))
+    return 2 * nbytes / (float(np.median(cms[1:])) * 1e-3) / 1e9
+
+
+def bench_rmsnorm(args) -> None:
+    """RMSNorm forward + backward (ce_rmsnorm_forward, ce_rmsnorm_backward):
+    one step = one forward call and one backward call over the whole batch,
+    inputs resident in HBM, L2 and MALL flushed before each call.  Roofline:
+    the backward call (its two kernels) against HBM peak."""
+    import torch
+    import cross_entropy_loss_amd as ce
+    import workloads as wl
+    nw = wl.NORM_WORKLOADS[args.workload if args.workload in wl.NORM_WORKLOADS else 1]
+    x, w, dy = wl.norm_inputs(nw)
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[nw.dtype]
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16) if nw.elem_bytes == 2 else a.view(np.int32)).to(dev).view(tdt)
+
+    xd, wd, dyd = to_dev(x), to_dev(w), to_dev(dy)
+    ws = torch.empty(ce.ce_rmsnorm_workspace_bytes(nw.N, nw.H, tdt), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        flush.fill_(2 * i)
+        if ev:
+            ev[0].record(stream)
+        y, rstd = ce.ce_rmsnorm_forward(xd, wd, nw.eps)
+        if ev:
+            ev[1].record(stream)
+        flush.fill_(2 * i + 1)
+        if ev:
+            ev[2].record(stream)
+        dx, dw = ce.ce_rmsnorm_backward(dyd, xd, wd, rstd, workspace=ws)
+        if ev:
+            ev[3].record(stream)
+        return y, dx, dw
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    copy_gbs = _calib_copy_gbs(xd, torch.empty_like(xd), nw.N * nw.H * nw.elem_bytes, flush, stream,
+                               3 if args.calibrate else 7)
+    ab = norm_bytes(nw)
+    step_ms = float(fwd.mean() + bwd.mean())
+    bw_gbs = ab["backward"] / (float(bwd.mean()) * 1e-3) / 1e9
+    fw_gbs = ab["forward"] / (float(fwd.mean()) * 1e-3) / 1e9
+    traffic = None
+    p = os.path.join(ROOT, "profiles", f"rmsnorm_{nw.name}.counters.json")
+    if os.path.exists(p):
+        with open(p) as f:
+            c = json.load(f)
+        if c.get("kernel_sha") == kernel_sha(NORM_SOURCES):
+            traffic = c.get("backward_traffic_bytes")
+    rec = {
+        "metric": f"RMSNorm fwd+bwd tokens/s and HBM GB/s (% of peak), N={nw.N} H={nw.H} {nw.dtype}",
+        "value": nw.N / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": nw.dtype, "data": "synthetic",
+        "config": {"workload": nw.name, "rows": nw.N, "hidden": nw.H, "eps": nw.eps, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "backward call: rms_bwd16 + rms_dw_reduce", "achieved": bw_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": bw_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "copy_ceiling": copy_gbs, "frac_of_copy": bw_gbs / copy_gbs},
+        "timing": {"forward_ms_mean": float(fwd.mean()), "forward_ms_median": float(np.median(fwd)),
+                   "forward_gbs": fw_gbs, "backward_ms_mean": float(bwd.mean()),
+                   "backward_ms_median": float(np.median(bwd)), "algorithmic_bytes": ab,
+                   "wall_ms_per_step_incl_flush": wall / args.steps * 1e3, "kernel_sha": kernel_sha(NORM_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rmsnorm as orn
+        rows, done, t0 = 256, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 8.0:
+            orn.rmsnorm(x[:rows], w, nw.dtype, nw.eps, dy[:rows])
+            done += rows
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {rows} rows of {nw.name}, float64 forward + backward (numpy, "
+                                         f"one thread), {done // rows} passes, {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,13 +534,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR")
-    ap.add_argument("--op", choices=["ce", "linear"], default="ce",
-                    help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy")
+    ap.add_argument("--op", choices=["ce", "linear", "rmsnorm"], default="ce",
+                    help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy; "
+                         "rmsnorm: RMS layer normalisation forward + backward")
     ap.add_argument("--chunk-rows", type=int, default=None, help="--op linear: rows per chunk")
     args = ap.parse_args()
     if args.profile_summary:
         if args.op == "linear":
             profile_summary_linear(args.profile_summary, args.workload)
+        elif args.op == "rmsnorm":
+            profile_summary_norm(args.profile_summary, args.workload)
         else:
             profile_summary(args.profile_summary, args.workload)
         return
@@ -342,6 +553,9 @@ def main():
         sys.exit(2)
     if args.op == "linear":
         bench_linear(args)
+        return
+    if args.op == "rmsnorm":
+        bench_rmsnorm(args)
         return
 
     import torch

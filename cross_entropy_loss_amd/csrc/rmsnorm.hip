@@ -15,43 +15,34 @@
 //
 // Shape of the work.  HBM-bound rows of a few KB (Mistral-7B: H = 4096 bf16,
 // 8 KB): one wave per row, the row in VGPRs (VPL 16-byte vectors per lane),
-// sums of squares and dot products reduced with DPP lane moves, no LDS and no
-// barrier on the row path.  The backward's dw is summed without atomics: each
-// wave keeps per-lane fp32 sums over the rows it handles, the four waves of a
-// workgroup are added in a fixed order through LDS, and a second launch adds
-// the workgroups' partials in a fixed order (deterministic).
+// sums of squares and dot products reduced with DPP lane moves, no barrier on
+// the row path.  Rows are read and written through buffer resources (one per
+// row, in SGPRs): loads past the row return 0 and stores past it are dropped,
+// so the row path has no per-vector branches (a branch per vector made the
+// compiler wait for every earlier store before each store).  The backward's
+// dw is summed without atomics: each wave keeps per-lane fp32 sums over the
+// rows it handles, the workgroup's waves are added in a fixed order through
+// LDS, and a second launch adds the workgroups' partials in a fixed order
+// (deterministic).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "ce_buffer.h"
 #include "ce_mi355x.h"
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using cek::buf_store;
+using cek::row_rsrc;
+using cek::u32x4;
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;          // waves (rows in flight) per workgroup
-constexpr int kMaxBwdGroups = 256; // backward workgroups: partial rows of dw
-constexpr int kMaxVPL = 32;     // forward: rows up to 32 KB (16384 bf16 / 8192 fp32)
-constexpr int kMaxBwdVPL = 8;   // backward: the per-lane dw sums (8 VPL floats) stay in VGPRs
-
-// Waves per SIMD the register budget must allow (without a bound the
-// compiler has taken up to 256 VGPRs for these shapes, one wave per SIMD).
-template <int VPL>
-constexpr int fwd_min_waves() { return VPL <= 8 ? 8 : (VPL <= 16 ? 4 : 2); }
-template <int VPL>
-constexpr int bwd_min_waves() { return VPL <= 4 ? 4 : 3; }
-
-// Makes the compiler treat v as redefined here, so that values it derived
-// from v earlier (unpacked floats) are recomputed rather than kept live
-// across the two passes over the row.
-__device__ __forceinline__ void fence_regs(u32x4& v) { asm volatile("" : "+v"(v)); }
-
+// 16-bit element formats: the two halves of a 32-bit word as floats, and two
+// floats rounded (to nearest even) into one word.  Words are taken by value.
 struct BF16 {
-  static constexpr int EPV = 8;
   __device__ static float lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
   __device__ static float hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
   __device__ static uint32_t pack(float a, float b) {
@@ -60,7 +51,6 @@ struct BF16 {
   }
 };
 struct F16 {
-  static constexpr int EPV = 8;
   __device__ static float lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u).x; }
   __device__ static float hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u).y; }
   __device__ static uint32_t pack(float a, float b) {
@@ -69,7 +59,54 @@ struct F16 {
   }
 };
 
+constexpr int kWaves = 4;          // forward: waves (rows in flight) per workgroup
+#ifndef RMS_BWD_WAVES
+#define RMS_BWD_WAVES 8
+#endif
+#ifndef RMS_BWD_GROUPS
+#define RMS_BWD_GROUPS 256
+#endif
+constexpr int kBwdWaves = RMS_BWD_WAVES;       // backward: waves per workgroup (one per row in flight)
+constexpr int kMaxBwdGroups = RMS_BWD_GROUPS;  // backward workgroups: partial rows of dw
+constexpr int kMaxVPL = 32;     // forward: rows up to 32 KB (16384 bf16 / 8192 fp32)
+constexpr int kMaxBwdVPL = 8;   // backward: the per-lane dw sums (8 VPL floats) stay in VGPRs
+constexpr int kNT = 2;          // buffer instruction aux bits: nontemporal (streamed rows)
+
+// Waves per SIMD the register budget must allow (without a bound the
+// compiler has taken up to 256 VGPRs for these shapes, one wave per SIMD).
+template <int VPL>
+constexpr int fwd_min_waves() { return VPL <= 4 ? 8 : (VPL <= 8 ? 6 : (VPL <= 16 ? 4 : 2)); }
+template <int VPL>
+constexpr int bwd_min_waves() { return VPL <= 4 ? 4 : 3; }
+
+// Makes the compiler treat v as redefined here, so that values it derived
+// from v earlier (unpacked floats) are recomputed rather than kept live
+// across the two passes over the row.
+__device__ __forceinline__ void fence_regs(u32x4& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ u32x4 ld_vec(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int k) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k * 1024, kNT));
+}
+// A row of `bytes` bytes at p; p is wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* p, uint32_t bytes) {
+  return row_rsrc(p, bytes);
+}
+// The weight row into LDS, once per workgroup, zero past its nvec vectors (so
+// lanes past the row read a zero weight); ends with a barrier.  LDS reads
+// count on their own counter, so reading the weight between a row's stores
+// does not make each store wait for the ones before it, as a global load
+// there would.
+template <int VPL>
+__device__ __forceinline__ void stage_weight(const char* w, int nvec, u32x4 (&lw)[VPL * 64]) {
+  const u32x4* wr = (const u32x4*)w;
+  for (int i = threadIdx.x; i < VPL * 64; i += blockDim.x) lw[i] = i < nvec ? wr[i] : u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+}
+
+// The row index of this wave, in a scalar register.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // Wave sum on DPP lane moves (quad_perm, row mirrors, row broadcasts); the
 // wave's sum is read from lane 63.
@@ -97,31 +134,30 @@ __device__ __forceinline__ double wave_sum(double v) {
 // Forward, 16-bit formats: one wave per row.
 // ---------------------------------------------------------------------------
 template <typename T, int VPL>
-__global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd16(const char* x, int64_t ldx, const char* w, int64_t N, int H,
-                                                         float eps, char* y, int64_t ldy, float* rstd_out) {
+__global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd16(const char* x, int64_t ldx,
+                                                                                const char* w, int64_t N, int H,
+                                                                                float eps, char* y, int64_t ldy,
+                                                                                float* rstd_out) {
+  __shared__ u32x4 lw[VPL * 64];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave_id();
+  stage_weight<VPL>(w, H / 8, lw);
   if (row >= N) return;  // the whole wave
-  const u32x4* xr = (const u32x4*)(x + row * ldx * 2);
-  const u32x4* wr = (const u32x4*)w;
-  u32x4* yr = (u32x4*)(y + row * ldy * 2);
-  const int nvec = H / 8;
+  const uint32_t rb = (uint32_t)H * 2, voff = (uint32_t)lane * 16;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + row * ldx * 2, rb), ry = rsrc(y + row * ldy * 2, rb);
   u32x4 v[VPL];
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int i = k * 64 + lane;
-    if (i < nvec) v[k] = __builtin_nontemporal_load(xr + i);
-  }
+  for (int k = 0; k < VPL; ++k) v[k] = ld_vec(rx, voff, k);
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
   float ss = 0.0f;
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
-    if (k * 64 + lane < nvec)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float a = T::lo(v[k][d]), b = T::hi(v[k][d]);
-        ss = __builtin_fmaf(a, a, ss);
-        ss = __builtin_fmaf(b, b, ss);
-      }
+    for (int d = 0; d < 4; ++d) {
+      const float a = T::lo(v[k][d]), b = T::hi(v[k][d]);
+      ss = __builtin_fmaf(a, a, ss);
+      ss = __builtin_fmaf(b, b, ss);
+    }
   ss = wave_sum(ss);
   double ssd = (double)ss;
   if (!(ss <= 0x1p+120f) || ss < 0x1p-100f) {
@@ -130,13 +166,12 @@ __global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd16
     double s2 = 0.0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
-      if (k * 64 + lane < nvec)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const double a = (double)T::lo(v[k][d]), b = (double)T::hi(v[k][d]);
-          s2 = fma(a, a, s2);
-          s2 = fma(b, b, s2);
-        }
+      for (int d = 0; d < 4; ++d) {
+        const double a = (double)T::lo(v[k][d]), b = (double)T::hi(v[k][d]);
+        s2 = fma(a, a, s2);
+        s2 = fma(b, b, s2);
+      }
     ssd = wave_sum(s2);
   }
   const float r = (float)(1.0 / sqrt(ssd / (double)H + (double)eps));
@@ -144,107 +179,145 @@ __global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd16
   for (int k = 0; k < VPL; ++k) fence_regs(v[k]);
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
-    const int i = k * 64 + lane;
-    if (i < nvec) {
-      const u32x4 wv = wr[i];
-      u32x4 o;
+    const u32x4 wv = lw[k * 64 + lane];
+    u32x4 o;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        o[d] = T::pack(T::lo(v[k][d]) * r * T::lo(wv[d]), T::hi(v[k][d]) * r * T::hi(wv[d]));
-      __builtin_nontemporal_store(o, yr + i);
-    }
+    for (int d = 0; d < 4; ++d)
+      o[d] = T::pack(T::lo(v[k][d]) * r * T::lo(wv[d]), T::hi(v[k][d]) * r * T::hi(wv[d]));
+    buf_store<kNT>(o, ry, voff, k * 1024);
   }
   if (lane == 0) rstd_out[row] = r;
 }
 
 // Forward, fp32 rows: fp64 arithmetic, one rounding.
 template <int VPL>
-__global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd32(const char* x, int64_t ldx, const char* w, int64_t N, int H,
-                                                         float eps, char* y, int64_t ldy, float* rstd_out) {
+__global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd32(const char* x, int64_t ldx,
+                                                                                const char* w, int64_t N, int H,
+                                                                                float eps, char* y, int64_t ldy,
+                                                                                float* rstd_out) {
+  __shared__ u32x4 lw[VPL * 64];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave_id();
+  stage_weight<VPL>(w, H / 4, lw);
   if (row >= N) return;
-  const u32x4* xr = (const u32x4*)(x + row * ldx * 4);
-  const u32x4* wr = (const u32x4*)w;
-  u32x4* yr = (u32x4*)(y + row * ldy * 4);
-  const int nvec = H / 4;
+  const uint32_t rb = (uint32_t)H * 4, voff = (uint32_t)lane * 16;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + row * ldx * 4, rb), ry = rsrc(y + row * ldy * 4, rb);
   u32x4 v[VPL];
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int i = k * 64 + lane;
-    if (i < nvec) v[k] = __builtin_nontemporal_load(xr + i);
-  }
+  for (int k = 0; k < VPL; ++k) v[k] = ld_vec(rx, voff, k);
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
-    if (k * 64 + lane < nvec)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const double a = (double)as_f(v[k][d]);
-        ss = fma(a, a, ss);
-      }
+    for (int d = 0; d < 4; ++d) {
+      const double a = (double)as_f(v[k][d]);
+      ss = fma(a, a, ss);
+    }
   ss = wave_sum(ss);
   const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
 #pragma unroll
   for (int k = 0; k < VPL; ++k) fence_regs(v[k]);
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
-    const int i = k * 64 + lane;
-    if (i < nvec) {
-      const u32x4 wv = wr[i];
-      u32x4 o;
+    const u32x4 wv = lw[k * 64 + lane];
+    u32x4 o;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        o[d] = __builtin_bit_cast(uint32_t, (float)((double)as_f(v[k][d]) * r * (double)as_f(wv[d])));
-      __builtin_nontemporal_store(o, yr + i);
-    }
+    for (int d = 0; d < 4; ++d)
+      o[d] = __builtin_bit_cast(uint32_t, (float)((double)as_f(v[k][d]) * r * (double)as_f(wv[d])));
+    buf_store<kNT>(o, ry, voff, k * 1024);
   }
   if (lane == 0) rstd_out[row] = (float)r;
 }
 
 // ---------------------------------------------------------------------------
-// Backward: each wave takes rows blockIdx.x * kWaves + wave, + gridDim.x *
-// kWaves, ...; dx is written per row; per-lane fp32 sums of dy x^ over those
-// rows are added across the four waves in a fixed order (LDS, H floats) and
-// written as the workgroup's partial row of dw.
+// Backward: each wave takes rows blockIdx.x * kBwdWaves + wave, + gridDim.x *
+// kBwdWaves, ...; dx is written per row; per-lane fp32 sums of dy x^ over
+// those rows are added across the workgroup's waves in a fixed order through
+// LDS and written as the workgroup's partial row of dw.  Lanes past the row
+// load zeros (and a zero weight), so they add nothing to the sums.
+//
+// LDS: the weight row (static, staged once), and the running dw sums laid out
+// [vector k][quad q][lane][4] with compile-time strides, so a wave moves its
+// sums with 16-byte LDS accesses that the compiler can batch (with a runtime
+// stride it could not prove the addresses apart and waited out every
+// read-add-write in turn).  Waves 0 .. W-2 add into LDS in order; the last
+// wave adds the total to its own sums in registers and writes the partial
+// row straight to memory: ((s0 + s1) + ...) + s(W-1), a fixed order.
 // ---------------------------------------------------------------------------
+template <int VPL, int EPV>
+constexpr size_t bwd_lds_floats() { return (size_t)VPL * 64 * EPV; }
+
+template <int EPV, int VPL>
+__device__ __forceinline__ void merge_store(float (&acc)[VPL][EPV], float* la, int nvec, float* partial_row,
+                                            int lane, int wid) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int Q = EPV / 4;
+  f4* l4 = (f4*)la;
+  for (int wv = 0; wv < kBwdWaves - 1; ++wv) {
+    if (wid == wv) {
+      f4 t[VPL][Q];
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) t[k][q] = wv == 0 ? f4{0.f, 0.f, 0.f, 0.f} : l4[(k * Q + q) * 64 + lane];
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const f4 a = {acc[k][4 * q], acc[k][4 * q + 1], acc[k][4 * q + 2], acc[k][4 * q + 3]};
+          l4[(k * Q + q) * 64 + lane] = t[k][q] + a;
+        }
+    }
+    __syncthreads();
+  }
+  if (wid == kBwdWaves - 1) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int i = k * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const f4 a = {acc[k][4 * q], acc[k][4 * q + 1], acc[k][4 * q + 2], acc[k][4 * q + 3]};
+        const f4 tot = kBwdWaves > 1 ? l4[(k * Q + q) * 64 + lane] + a : a;
+        if (i < nvec) *(f4*)(partial_row + (size_t)i * EPV + 4 * q) = tot;
+      }
+    }
+  }
+}
+
 template <typename T, int VPL>
-__global__ __launch_bounds__(64 * kWaves, (bwd_min_waves<VPL>())) void rms_bwd16(const char* dy, int64_t lddy, const char* x, int64_t ldx,
-                                                         const char* w, const float* rstd, int64_t N, int H,
-                                                         char* dx, int64_t lddx, float* partial) {
-  extern __shared__ float lds_acc[];  // H floats
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd16(
+    const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
+    char* dx, int64_t lddx, float* partial) {
+  __shared__ float lds_acc[bwd_lds_floats<VPL, 8>()];
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int nvec = H / 8;
-  const u32x4* wr = (const u32x4*)w;
+  const uint32_t rb = (uint32_t)H * 2, voff = (uint32_t)lane * 16;
+  __shared__ u32x4 lw[VPL * 64];
+  stage_weight<VPL>(w, nvec, lw);
   float acc[VPL][8];
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.0f;
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + wid; row < N; row += (int64_t)gridDim.x * kWaves) {
-    const u32x4* gr = (const u32x4*)(dy + row * lddy * 2);
-    const u32x4* xr = (const u32x4*)(x + row * ldx * 2);
+  for (int64_t row = (int64_t)blockIdx.x * kBwdWaves + wid; row < N; row += (int64_t)gridDim.x * kBwdWaves) {
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 2, rb), rx = rsrc(x + row * ldx * 2, rb);
     u32x4 g[VPL], xv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        g[k] = __builtin_nontemporal_load(gr + i);
-        xv[k] = __builtin_nontemporal_load(xr + i);
-      }
+      g[k] = ld_vec(rg, voff, k);
+      xv[k] = ld_vec(rx, voff, k);
     }
+    __builtin_amdgcn_sched_barrier(0);
     const float r = rstd[row];
     float dot = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        const u32x4 wv = wr[i];
+      const u32x4 wv = lw[k * 64 + lane];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          dot = __builtin_fmaf(T::lo(xv[k][d]) * r, T::lo(wv[d]) * T::lo(g[k][d]), dot);
-          dot = __builtin_fmaf(T::hi(xv[k][d]) * r, T::hi(wv[d]) * T::hi(g[k][d]), dot);
-        }
+      for (int d = 0; d < 4; ++d) {
+        dot = __builtin_fmaf(T::lo(xv[k][d]) * r, T::lo(wv[d]) * T::lo(g[k][d]), dot);
+        dot = __builtin_fmaf(T::hi(xv[k][d]) * r, T::hi(wv[d]) * T::hi(g[k][d]), dot);
       }
     }
     const float c = wave_sum(dot) / (float)H;
@@ -253,81 +326,58 @@ __global__ __launch_bounds__(64 * kWaves, (bwd_min_waves<VPL>())) void rms_bwd16
       fence_regs(g[k]);
       fence_regs(xv[k]);
     }
-    u32x4* outr = (u32x4*)(dx + row * lddx * 2);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 2, rb);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        const u32x4 wv = wr[i];
-        u32x4 o;
+      const u32x4 wv = lw[k * 64 + lane];
+      u32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float xl = T::lo(xv[k][d]) * r, xh = T::hi(xv[k][d]) * r;
-          const float gl = T::lo(g[k][d]), gh = T::hi(g[k][d]);
-          o[d] = T::pack(r * (T::lo(wv[d]) * gl - xl * c), r * (T::hi(wv[d]) * gh - xh * c));
-          acc[k][2 * d] = __builtin_fmaf(gl, xl, acc[k][2 * d]);
-          acc[k][2 * d + 1] = __builtin_fmaf(gh, xh, acc[k][2 * d + 1]);
-        }
-        __builtin_nontemporal_store(o, outr + i);
+      for (int d = 0; d < 4; ++d) {
+        const float xl = T::lo(xv[k][d]) * r, xh = T::hi(xv[k][d]) * r;
+        const float gl = T::lo(g[k][d]), gh = T::hi(g[k][d]);
+        o[d] = T::pack(r * (T::lo(wv[d]) * gl - xl * c), r * (T::hi(wv[d]) * gh - xh * c));
+        acc[k][2 * d] = __builtin_fmaf(gl, xl, acc[k][2 * d]);
+        acc[k][2 * d + 1] = __builtin_fmaf(gh, xh, acc[k][2 * d + 1]);
       }
+      buf_store<kNT>(o, ro, voff, k * 1024);
     }
   }
-  // the four waves' sums, added in wave order
-  for (int wv = 0; wv < kWaves; ++wv) {
-    if (wid == wv) {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int i = k * 64 + lane;
-        if (i < nvec)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = i * 8 + e;
-            lds_acc[j] = (wv == 0 ? 0.0f : lds_acc[j]) + acc[k][e];
-          }
-      }
-    }
-    __syncthreads();
-  }
-  for (int j = threadIdx.x; j < H; j += 64 * kWaves) partial[(int64_t)blockIdx.x * H + j] = lds_acc[j];
+  merge_store(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, wid);
 }
 
 // Backward, fp32 rows: y-side arithmetic in fp64, the dw sums in fp32.
 template <int VPL>
-__global__ __launch_bounds__(64 * kWaves, (bwd_min_waves<VPL>())) void rms_bwd32(const char* dy, int64_t lddy, const char* x, int64_t ldx,
-                                                         const char* w, const float* rstd, int64_t N, int H,
-                                                         char* dx, int64_t lddx, float* partial) {
-  extern __shared__ float lds_acc[];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd32(
+    const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
+    char* dx, int64_t lddx, float* partial) {
+  __shared__ float lds_acc[bwd_lds_floats<VPL, 4>()];
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int nvec = H / 4;
-  const u32x4* wr = (const u32x4*)w;
+  const uint32_t rb = (uint32_t)H * 4, voff = (uint32_t)lane * 16;
+  __shared__ u32x4 lw[VPL * 64];
+  stage_weight<VPL>(w, nvec, lw);
   float acc[VPL][4];
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[k][e] = 0.0f;
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + wid; row < N; row += (int64_t)gridDim.x * kWaves) {
-    const u32x4* gr = (const u32x4*)(dy + row * lddy * 4);
-    const u32x4* xr = (const u32x4*)(x + row * ldx * 4);
+  for (int64_t row = (int64_t)blockIdx.x * kBwdWaves + wid; row < N; row += (int64_t)gridDim.x * kBwdWaves) {
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 4, rb), rx = rsrc(x + row * ldx * 4, rb);
     u32x4 g[VPL], xv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        g[k] = __builtin_nontemporal_load(gr + i);
-        xv[k] = __builtin_nontemporal_load(xr + i);
-      }
+      g[k] = ld_vec(rg, voff, k);
+      xv[k] = ld_vec(rx, voff, k);
     }
+    __builtin_amdgcn_sched_barrier(0);
     const double r = (double)rstd[row];
     double dot = 0.0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        const u32x4 wv = wr[i];
+      const u32x4 wv = lw[k * 64 + lane];
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-          dot = fma((double)as_f(xv[k][d]) * r, (double)as_f(wv[d]) * (double)as_f(g[k][d]), dot);
-      }
+      for (int d = 0; d < 4; ++d)
+        dot = fma((double)as_f(xv[k][d]) * r, (double)as_f(wv[d]) * (double)as_f(g[k][d]), dot);
     }
     const double c = wave_sum(dot) / (double)H;
 #pragma unroll
@@ -335,49 +385,69 @@ __global__ __launch_bounds__(64 * kWaves, (bwd_min_waves<VPL>())) void rms_bwd32
       fence_regs(g[k]);
       fence_regs(xv[k]);
     }
-    u32x4* outr = (u32x4*)(dx + row * lddx * 4);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 4, rb);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
-      if (i < nvec) {
-        const u32x4 wv = wr[i];
-        u32x4 o;
+      const u32x4 wv = lw[k * 64 + lane];
+      u32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const double xh = (double)as_f(xv[k][d]) * r, gd = (double)as_f(g[k][d]);
-          o[d] = __builtin_bit_cast(uint32_t, (float)(r * ((double)as_f(wv[d]) * gd - xh * c)));
-          acc[k][d] = __builtin_fmaf((float)gd, (float)xh, acc[k][d]);
-        }
-        __builtin_nontemporal_store(o, outr + i);
+      for (int d = 0; d < 4; ++d) {
+        const double xh = (double)as_f(xv[k][d]) * r, gd = (double)as_f(g[k][d]);
+        o[d] = __builtin_bit_cast(uint32_t, (float)(r * ((double)as_f(wv[d]) * gd - xh * c)));
+        acc[k][d] = __builtin_fmaf((float)gd, (float)xh, acc[k][d]);
       }
+      buf_store<kNT>(o, ro, voff, k * 1024);
     }
   }
-  for (int wv = 0; wv < kWaves; ++wv) {
-    if (wid == wv) {
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int i = k * 64 + lane;
-        if (i < nvec)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = i * 4 + e;
-            lds_acc[j] = (wv == 0 ? 0.0f : lds_acc[j]) + acc[k][e];
-          }
-      }
-    }
-    __syncthreads();
-  }
-  for (int j = threadIdx.x; j < H; j += 64 * kWaves) partial[(int64_t)blockIdx.x * H + j] = lds_acc[j];
+  merge_store(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, wid);
 }
 
-// dw[j] = sum over the G partial rows, in order, in fp64; rounded once.
+// dw[j] = sum over the G partial rows in fp64, rounded once.  A workgroup
+// takes 64 columns as 16 column quads; its 16 row slices (contiguous ranges
+// of the G rows) are summed by separate threads with all their 16-byte loads
+// in flight together, then added in slice order through LDS: a fixed order,
+// whatever the timing.  H is a multiple of 4.
+#ifndef RMS_RED_QUADS
+#define RMS_RED_QUADS 16
+#endif
+constexpr int kRedQuads = RMS_RED_QUADS, kRedSlices = 256 / kRedQuads, kRedUnroll = 16;
 template <typename TO>
-__global__ __launch_bounds__(256) void rms_dw_reduce(const float* partial, int G, int H, TO* dw) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= H) return;
-  double s = 0.0;
-  for (int g = 0; g < G; ++g) s += (double)partial[(int64_t)g * H + j];
-  dw[j] = (TO)s;
+__global__ __launch_bounds__(kRedQuads * kRedSlices) void rms_dw_reduce(const float* partial, int G, int H, TO* dw) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ double part[kRedSlices][kRedQuads * 4];
+  const int cq = threadIdx.x % kRedQuads, sl = threadIdx.x / kRedQuads;
+  const int j = (blockIdx.x * kRedQuads + cq) * 4;
+  const int per = (G + kRedSlices - 1) / kRedSlices;
+  const int g0 = sl * per, g1 = min(G, g0 + per);
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  if (j < H) {
+    for (int g = g0; g < g1; g += kRedUnroll) {
+      f4 v[kRedUnroll];
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u)
+        v[u] = g + u < g1 ? *(const f4*)(partial + (int64_t)(g + u) * H + j) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u) {
+        s0 += (double)v[u].x;
+        s1 += (double)v[u].y;
+        s2 += (double)v[u].z;
+        s3 += (double)v[u].w;
+      }
+    }
+  }
+  part[sl][cq * 4 + 0] = s0;
+  part[sl][cq * 4 + 1] = s1;
+  part[sl][cq * 4 + 2] = s2;
+  part[sl][cq * 4 + 3] = s3;
+  __syncthreads();
+  const int c = threadIdx.x;  // one output column per thread of the first 4 kRedQuads
+  const int jc = blockIdx.x * kRedQuads * 4 + c;
+  if (c < kRedQuads * 4 && jc < H) {
+    double t = part[0][c];
+#pragma unroll
+    for (int q = 1; q < kRedSlices; ++q) t += part[q][c];
+    dw[jc] = (TO)t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -397,7 +467,7 @@ int vpl_for(int64_t H, int dtype) {
 }
 
 int bwd_groups(int64_t N) {
-  const int64_t g = (N + kWaves - 1) / kWaves;
+  const int64_t g = (N + kBwdWaves - 1) / kBwdWaves;
   return (int)(g < 1 ? 1 : (g > kMaxBwdGroups ? kMaxBwdGroups : g));
 }
 
@@ -484,19 +554,19 @@ int ce_rmsnorm_backward(const void* dy, int64_t ld_dy, const void* x, int64_t ld
   float* partial = (float*)workspace;
   const int G = bwd_groups(N);
   if (N > 0) {
-    hipLaunchKernelGGL(bwd_fn(dtype, vpl), dim3((unsigned)G), dim3(64 * kWaves), (size_t)H * 4, st, (const char*)dy,
+    hipLaunchKernelGGL(bwd_fn(dtype, vpl), dim3((unsigned)G), dim3(64 * kBwdWaves), 0, st, (const char*)dy,
                        ld_dy, (const char*)x, ld_x, (const char*)weight, rstd, N, (int)H, (char*)dx, ld_dx, partial);
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   const int gsum = N > 0 ? G : 0;
-  const unsigned rb = (unsigned)((H + 255) / 256);
+  const unsigned rb = (unsigned)((H + kRedQuads * 4 - 1) / (kRedQuads * 4));
+  const dim3 rt(kRedQuads * kRedSlices);
   if (dtype == CE_DTYPE_BF16)
-    hipLaunchKernelGGL(rms_dw_reduce<__bf16>, dim3(rb), dim3(256), 0, st, partial, gsum, (int)H, (__bf16*)dweight);
+    hipLaunchKernelGGL(rms_dw_reduce<__bf16>, dim3(rb), rt, 0, st, partial, gsum, (int)H, (__bf16*)dweight);
   else if (dtype == CE_DTYPE_F16)
-    hipLaunchKernelGGL(rms_dw_reduce<_Float16>, dim3(rb), dim3(256), 0, st, partial, gsum, (int)H,
-                       (_Float16*)dweight);
+    hipLaunchKernelGGL(rms_dw_reduce<_Float16>, dim3(rb), rt, 0, st, partial, gsum, (int)H, (_Float16*)dweight);
   else
-    hipLaunchKernelGGL(rms_dw_reduce<float>, dim3(rb), dim3(256), 0, st, partial, gsum, (int)H, (float*)dweight);
+    hipLaunchKernelGGL(rms_dw_reduce<float>, dim3(rb), rt, 0, st, partial, gsum, (int)H, (float*)dweight);
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 

@@ -265,3 +265,36 @@ def linear_inputs(lw: LinearWorkload, threads: int | None = None):
     ign = rng.choice(lw.N, int(round(lw.ignore_frac * lw.N)), replace=False)
     y[ign] = IGNORE_INDEX
     return h, w, y
+
+
+@dataclasses.dataclass(frozen=True)
+class NormWorkload:
+    """RMSNorm over the hidden states: N token rows of H elements, a weight of
+    H elements and an upstream gradient of the output's shape."""
+    name: str
+    seed: int
+    N: int
+    H: int
+    dtype: str
+    eps: float = 1e-5
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+NORM_WORKLOADS = {
+    # a Mistral-7B decoder norm (hidden 4096, eps 1e-5) over batch 4 x sequence 1024
+    1: NormWorkload("mistral7b-rmsnorm-b4s1024-bf16", 8, 4096, 4096, "bf16"),
+}
+
+
+def norm_inputs(nw: NormWorkload, threads: int | None = None):
+    """(x [N, H], weight [H], dy [N, H]) storage arrays: x and dy iid N(0, 1),
+    the weight 1 + N(0, 0.25^2) (a trained norm's weights sit around one)."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    x = _normal_rows(nw.seed, 5, nw.N, nw.H, 1.0, nw.dtype, threads)
+    dy = _normal_rows(nw.seed, 6, nw.N, nw.H, 1.0, nw.dtype, threads)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((nw.seed, 7))))
+    w = to_storage(1.0 + 0.25 * rng.standard_normal(nw.H), nw.dtype)
+    return x, w, dy
