@@ -23,7 +23,7 @@ __all__ = [
     "ce_workspace_bytes", "ce_workspace_init", "Workspace", "ce_forward", "ce_backward",
     "ce_fwd_bwd_inplace", "cross_entropy", "FastCrossEntropyLoss", "CeError",
     "ce_linear_workspace_bytes", "ce_linear_fwd_bwd", "ce_rmsnorm_workspace_bytes", "ce_rmsnorm_forward",
-    "ce_rmsnorm_backward", "rms_norm", "FastRMSNorm",
+    "ce_rmsnorm_backward", "rms_norm", "FastRMSNorm", "ce_rope", "rope", "FastRoPE",
 ]
 
 _DTYPES = {torch.float32: _lib.CE_DTYPE_F32, torch.bfloat16: _lib.CE_DTYPE_BF16,
@@ -325,6 +325,92 @@ class FastRMSNorm(torch.nn.Module):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return rms_norm(x, self.weight, self.eps)
+
+
+def _heads_view(t: torch.Tensor, name: str):
+    """(tokens, heads, ld_token, ld_head) of a [tokens, heads, head_dim] view."""
+    if t.dim() != 3 or t.stride(2) != 1 or not t.is_cuda:
+        raise ValueError(f"{name} must be a [tokens, heads, head_dim] GPU tensor with contiguous head_dim")
+    return t.shape[0], t.shape[1], t.stride(0), t.stride(1)
+
+
+def ce_rope(q: torch.Tensor, k: torch.Tensor | None, positions: torch.Tensor, base: float = 10000.0,
+            inverse: bool = False, inplace: bool = False) -> tuple:
+    """Rotary embedding of q and k ([tokens, heads, head_dim] views) at the
+    tokens' positions (int64 [tokens]); returns (q_out, k_out), written over
+    q and k when inplace."""
+    T, Hq, ltq, lhq = _heads_view(q, "q")
+    D = q.shape[2]
+    if k is not None:
+        Tk, Hk, ltk, lhk = _heads_view(k, "k")
+        if Tk != T or k.shape[2] != D or k.dtype != q.dtype or k.device != q.device:
+            raise ValueError("k must match q in tokens, head_dim, dtype and device")
+    else:
+        Hk, ltk, lhk = 0, 0, 0
+    if positions.dtype != torch.int64 or positions.numel() != T or positions.device != q.device \
+            or (T > 1 and positions.stride(0) != 1):
+        raise ValueError("positions must be a contiguous int64 [tokens] tensor on q's device")
+
+    def out_like(t):
+        return t if inplace else torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+
+    qo = out_like(q)
+    ko = out_like(k) if k is not None else None
+    rc = _lib.load().ce_rope(_ptr(q), _ptr(qo), ltq, lhq, Hq, _ptr(k), _ptr(ko), ltk, lhk, Hk, _ptr(positions), T, D,
+                             float(base), int(inverse), _dtype_code(q), _stream(q.device))
+    _lib.check(rc, "ce_rope")
+    return qo, ko
+
+
+def _rope_any(x: torch.Tensor, positions: torch.Tensor, base: float, inverse: bool) -> torch.Tensor:
+    """x as [tokens, heads, D] or [batch, heads, seq, D] (positions [tokens] or
+    [batch, seq]); the 4-D layout runs one call per batch row, each writing
+    its slice of the output (same strides as x)."""
+    if x.dim() == 3:
+        return ce_rope(x, None, positions.reshape(-1), base, inverse)[0]
+    if x.dim() != 4:
+        raise ValueError("x must be [tokens, heads, head_dim] or [batch, heads, seq, head_dim]")
+    out = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, device=x.device)
+    pos = positions.reshape(x.shape[0], x.shape[2])
+    lib = _lib.load()
+    for b in range(x.shape[0]):
+        xb, ob = x[b].transpose(0, 1), out[b].transpose(0, 1)  # [seq, heads, D] views
+        T, H, lt, lh = _heads_view(xb, "x")
+        pb = pos[b].contiguous()
+        rc = lib.ce_rope(_ptr(xb), _ptr(ob), lt, lh, H, None, None, 0, 0, 0, _ptr(pb), T, x.shape[3], float(base),
+                         int(inverse), _dtype_code(x), _stream(x.device))
+        _lib.check(rc, "ce_rope")
+    return out
+
+
+class _RoPE(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, positions, base):
+        ctx.save_for_backward(positions)
+        ctx.base = base
+        return _rope_any(x, positions, base, False)
+
+    @staticmethod
+    def backward(ctx, dy):
+        (positions,) = ctx.saved_tensors
+        return _rope_any(dy.contiguous(), positions, ctx.base, True), None, None
+
+
+def rope(x: torch.Tensor, positions: torch.Tensor, base: float = 10000.0) -> torch.Tensor:
+    """Rotary embedding with autograd: x [tokens, heads, D] with positions
+    [tokens], or [batch, heads, seq, D] with positions [batch, seq]."""
+    return _RoPE.apply(x, positions, base)
+
+
+class FastRoPE(torch.nn.Module):
+    """Applies the rotary embedding to q and k at explicit position ids."""
+
+    def __init__(self, base: float = 10000.0):
+        super().__init__()
+        self.base = base
+
+    def forward(self, q: torch.Tensor, k: torch.Tensor, positions: torch.Tensor):
+        return rope(q, positions, self.base), rope(k, positions, self.base)
 
 
 class _CrossEntropy(torch.autograd.Function):

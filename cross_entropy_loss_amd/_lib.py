@@ -14,7 +14,7 @@ CE_DTYPE_F32, CE_DTYPE_BF16, CE_DTYPE_F16 = 0, 1, 2
 CE_OK, CE_ERR_INVALID_ARG, CE_ERR_DTYPE, CE_ERR_WORKSPACE, CE_ERR_UNSUPPORTED, CE_ERR_HIP = range(6)
 CE_STATUS_LABEL_RANGE = 0x1
 CE_STATUS_SYNC_TIMEOUT = 0x2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # every symbol the header declares, with its C signature
 _i64, _int, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -34,6 +34,8 @@ SIGNATURES = {
     "ce_rmsnorm_backward": ([_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _int, _vp, _i64, _vp, _vp, _sz, _vp], _int),
     "ce_linear_fwd_bwd": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                            _vp, _i64, _vp, _i64, _vp, _sz, _vp], _int),
+    "ce_rope": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, ctypes.c_double, _int,
+                 _int, _vp], _int),
 }
 
 _lib = None

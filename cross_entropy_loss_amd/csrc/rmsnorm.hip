@@ -30,34 +30,16 @@
 
 #include "ce_buffer.h"
 #include "ce_mi355x.h"
+#include "row_formats.h"
 
 namespace {
 
 using cek::buf_store;
 using cek::row_rsrc;
 using cek::u32x4;
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-
-// 16-bit element formats: the two halves of a 32-bit word as floats, and two
-// floats rounded (to nearest even) into one word.  Words are taken by value.
-struct BF16 {
-  __device__ static float lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
-  __device__ static float hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
-  __device__ static uint32_t pack(float a, float b) {
-    f2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
-  }
-};
-struct F16 {
-  __device__ static float lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u).x; }
-  __device__ static float hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u).y; }
-  __device__ static uint32_t pack(float a, float b) {
-    f2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
-  }
-};
+using rowfmt::as_f;
+using rowfmt::BF16;
+using rowfmt::F16;
 
 constexpr int kWaves = 4;          // forward: waves (rows in flight) per workgroup
 #ifndef RMS_BWD_WAVES
@@ -83,8 +65,6 @@ constexpr int bwd_min_waves() { return VPL <= 4 ? 4 : 3; }
 // from v earlier (unpacked floats) are recomputed rather than kept live
 // across the two passes over the row.
 __device__ __forceinline__ void fence_regs(u32x4& v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 __device__ __forceinline__ u32x4 ld_vec(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int k) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k * 1024, kNT));

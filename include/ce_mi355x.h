@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 3
+#define CE_ABI_VERSION 4
 
 /* element formats of logits and gradients */
 enum ce_dtype { CE_DTYPE_F32 = 0, CE_DTYPE_BF16 = 1, CE_DTYPE_F16 = 2 };
@@ -247,6 +247,41 @@ int ce_rmsnorm_forward(const void* x, int64_t ld_x, const void* weight, int64_t 
 int ce_rmsnorm_backward(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* weight,
                         const float* rstd, int64_t n_rows, int64_t hidden, int dtype, void* dx, int64_t ld_dx,
                         void* dweight, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Rotary position embedding with per-token position ids.
+ *
+ * The pages list "Fast RoPE" among the package's kernels (PyPI page
+ * "fms-acceleration-foak 0.7.4", kernel list) and note that it takes no
+ * position ids (same page, known issues; fms-hf-tuning PR #280, "Notes on
+ * FastKernels"); padding-free packed batches need them (positions restart at
+ * each packed sequence).  For token t at position p = positions[t] and every
+ * head of q and k, with D = head_dim and pairs i = 0 .. D/2-1 formed by
+ * elements i and i + D/2:
+ *
+ *   theta = p * base^(-2 i / D)     (negated when inverse = 1)
+ *   y_i       = x_i cos(theta) - x_{i+D/2} sin(theta)
+ *   y_{i+D/2} = x_{i+D/2} cos(theta) + x_i sin(theta)
+ *
+ * inverse = 1 is the rotation back, i.e. the backward: dq = rope(dq_out, -theta).
+ * q: q_heads heads of head_dim elements per token, element (t, h, j) at
+ * q + (t * q_ld_token + h * q_ld_head + j) * element size; q_out has the same
+ * strides and may be q itself (in place); likewise k (k_heads = 0: no k, the
+ * pointers may be NULL).  positions: n_tokens int64 values.  Angles are
+ * computed in fp64; 16-bit formats rotate in fp32 and round once, fp32 data
+ * rotates in fp64.  The (token, head) segments must not overlap
+ * (CE_ERR_INVALID_ARG).  Served: head_dim / 2 a multiple of 8 (16-bit) or 4
+ * (fp32) and head_dim <= 256; pointers and strides * element size multiples of
+ * 16 bytes; one token's heads spanning under 2 GiB (else CE_ERR_UNSUPPORTED).
+ * Errors: CE_ERR_DTYPE, CE_ERR_INVALID_ARG (negative sizes, odd or < 2
+ * head_dim, base not finite and positive, inverse not 0/1, NULL pointers,
+ * overlapping segments), CE_ERR_UNSUPPORTED, CE_ERR_HIP; nothing is written on
+ * an error return.  n_tokens = 0 (or no heads) returns CE_OK without reading any
+ * pointer.  One kernel launch on `stream`; nothing is allocated.
+ */
+int ce_rope(const void* q, void* q_out, int64_t q_ld_token, int64_t q_ld_head, int64_t q_heads, const void* k,
+            void* k_out, int64_t k_ld_token, int64_t k_ld_head, int64_t k_heads, const int64_t* positions,
+            int64_t n_tokens, int64_t head_dim, double base, int inverse, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -266,3 +266,44 @@ def test_rmsnorm_forward_rejects(lib, kw, code):
 ])
 def test_rmsnorm_backward_rejects(lib, kw, code):
     assert rms_bwd(lib, **kw) == code
+
+
+def rope_call(lib, q=FAKE, qo=FAKE + 4096, ltq=32 * 128, lhq=128, hq=32, k=FAKE + 8192, ko=FAKE + 8192, ltk=8 * 128,
+              lhk=128, hk=8, pos=FAKE, T=16, D=128, base=10000.0, inverse=0, dtype=1):
+    return lib.ce_rope(VP(q), VP(qo), ltq, lhq, hq, VP(k), VP(ko), ltk, lhk, hk, VP(pos), T, D, base, inverse, dtype,
+                       None)
+
+
+def test_rope_empty_calls_are_no_ops(lib):
+    # nothing is launched, so the fake pointers are never touched
+    assert rope_call(lib, T=0) == _lib.CE_OK
+    assert rope_call(lib, hq=0, hk=0, q=0, qo=0, k=0, ko=0) == _lib.CE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.CE_ERR_DTYPE),
+    (dict(T=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(hq=-1), _lib.CE_ERR_INVALID_ARG),
+    (dict(D=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(D=127), _lib.CE_ERR_INVALID_ARG),
+    (dict(base=0.0), _lib.CE_ERR_INVALID_ARG),
+    (dict(base=-10.0), _lib.CE_ERR_INVALID_ARG),
+    (dict(base=float("inf")), _lib.CE_ERR_INVALID_ARG),
+    (dict(base=float("nan")), _lib.CE_ERR_INVALID_ARG),
+    (dict(inverse=2), _lib.CE_ERR_INVALID_ARG),
+    (dict(pos=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(q=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(qo=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(ko=0), _lib.CE_ERR_INVALID_ARG),
+    (dict(lhq=64), _lib.CE_ERR_INVALID_ARG),            # heads overlap (stride below head_dim)
+    (dict(ltq=31 * 128), _lib.CE_ERR_INVALID_ARG),      # tokens overlap
+    (dict(ltk=-128), _lib.CE_ERR_INVALID_ARG),
+    (dict(D=24, lhq=24, ltq=32 * 24, lhk=24, ltk=8 * 24), _lib.CE_ERR_UNSUPPORTED),  # 12 pairs: not 8-aligned
+    (dict(D=272, lhq=272, ltq=32 * 272, lhk=272, ltk=8 * 272), _lib.CE_ERR_UNSUPPORTED),  # over 128 pairs
+    (dict(dtype=0, D=12, lhq=12, ltq=32 * 12, lhk=12, ltk=8 * 12), _lib.CE_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), _lib.CE_ERR_UNSUPPORTED),
+    (dict(lhq=132, ltq=32 * 132), _lib.CE_ERR_UNSUPPORTED),  # 264-byte head stride
+    (dict(hq=1 << 20, lhq=1 << 12, ltq=(1 << 32)), _lib.CE_ERR_UNSUPPORTED),  # one token's heads over 2 GiB
+])
+def test_rope_rejects(lib, kw, code):
+    assert rope_call(lib, **kw) == code

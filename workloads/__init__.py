@@ -298,3 +298,50 @@ def norm_inputs(nw: NormWorkload, threads: int | None = None):
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((nw.seed, 7))))
     w = to_storage(1.0 + 0.25 * rng.standard_normal(nw.H), nw.dtype)
     return x, w, dy
+
+
+@dataclasses.dataclass(frozen=True)
+class RopeWorkload:
+    """Rotary embedding of one attention layer's q and k over a padding-free
+    packed batch: T tokens, Hq query heads and Hk key heads of head_dim D;
+    positions restart at every packed sequence (lengths uniform in
+    [min_len, max_len], the last one cut at T)."""
+    name: str
+    seed: int
+    T: int
+    Hq: int
+    Hk: int
+    D: int
+    dtype: str
+    base: float = 10000.0
+    min_len: int = 64
+    max_len: int = 1024
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+ROPE_WORKLOADS = {
+    # Mistral-7B attention: 32 query heads, 8 key heads, head_dim 128, rope base 10000
+    1: RopeWorkload("mistral7b-rope-packed4096-bf16", 9, 4096, 32, 8, 128, "bf16"),
+}
+
+
+def packed_positions(seed: int, T: int, min_len: int, max_len: int) -> np.ndarray:
+    """Positions of a packed batch: 0, 1, ... restarting at each sequence."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((seed, 10))))
+    out, n = [], 0
+    while n < T:
+        L = int(min(rng.integers(min_len, max_len + 1), T - n))
+        out.append(np.arange(L, dtype=np.int64))
+        n += L
+    return np.concatenate(out)
+
+
+def rope_inputs(rw: RopeWorkload, threads: int | None = None):
+    """(q [T, Hq, D], k [T, Hk, D], positions [T]) storage arrays, q and k iid N(0, 1)."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    q = _normal_rows(rw.seed, 11, rw.T, rw.Hq * rw.D, 1.0, rw.dtype, threads).reshape(rw.T, rw.Hq, rw.D)
+    k = _normal_rows(rw.seed, 12, rw.T, rw.Hk * rw.D, 1.0, rw.dtype, threads).reshape(rw.T, rw.Hk, rw.D)
+    return q, k, packed_positions(rw.seed, rw.T, rw.min_len, rw.max_len)
