@@ -46,7 +46,8 @@ KERNEL_SOURCES = ["cross_entropy_loss_amd/csrc/ce_kernels.h", "cross_entropy_los
                   "cross_entropy_loss_amd/csrc/ce_api.hip"]
 
 
-NORM_SOURCES = ["cross_entropy_loss_amd/csrc/rmsnorm.hip", "cross_entropy_loss_amd/csrc/ce_buffer.h"]
+NORM_SOURCES = ["cross_entropy_loss_amd/csrc/rmsnorm.hip", "cross_entropy_loss_amd/csrc/ce_buffer.h",
+                "cross_entropy_loss_amd/csrc/row_formats.h"]
 
 
 def kernel_sha(sources=KERNEL_SOURCES) -> str:
@@ -331,32 +332,16 @@ def norm_bytes(nw) -> dict:
     return {"forward": 2 * N * H * e + H * e + 4 * N, "backward": 3 * N * H * e + 2 * H * e + 4 * N}
 
 
-NORM_KERNELS = ("rms_fwd", "rms_bwd", "rms_dw_reduce")
-
-
-def profile_summary_norm(d: str, workload: int) -> None:
-    """rocprofv3 databases of bench.py --op rmsnorm runs -> profiles/rmsnorm_<workload>.txt
-    and the counters JSON that bench.py reads for roofline.traffic (the
-    backward call: rms_bwd* + rms_dw_reduce)."""
+def _summarize(d: str, stem: str, header: list, parts: dict, calib_bytes: int, sha: str) -> dict:
+    """rocprofv3 databases under d (trace_results.db, fetch_results.db,
+    write_results.db) -> profiles/<stem>.txt and, with counters, the
+    <stem>.counters.json that bench.py reads for roofline.traffic.
+    parts: name -> (kernel-name substrings, algorithmic bytes of that call)."""
     import glob
-    import workloads as wl
-    workload = workload if workload in wl.NORM_WORKLOADS else 1
-    nw = wl.NORM_WORKLOADS[workload]
-    find = lambda stem: (glob.glob(os.path.join(d, "**", f"{stem}_results.db"), recursive=True) or [None])[0]
+    find = lambda tag: (glob.glob(os.path.join(d, "**", f"{tag}_results.db"), recursive=True) or [None])[0]
     trace, fetch, write = find("trace"), find("fetch"), find("write")
-    ab = norm_bytes(nw)
-    sha = kernel_sha(NORM_SOURCES)
-    lines = [f"# rocprofv3 summary: RMSNorm forward and backward, workload {nw.name}",
-             f"# N={nw.N} H={nw.H} dtype={nw.dtype} eps={nw.eps}; kernel sources sha {sha}",
-             "# commands (from the repository root):",
-             "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
-             f"python bench.py --op rmsnorm --workload {workload} --steps 10 --no-cpu-baseline",
-             "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- "
-             f"python bench.py --op rmsnorm --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
-             "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- "
-             f"python bench.py --op rmsnorm --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
-             f"#   python bench.py --op rmsnorm --profile-summary D --workload {workload}", ""]
-    rec = {"kernel_sha": sha, "workload": nw.name, "algorithmic_bytes": ab}
+    lines = list(header)
+    rec = {"kernel_sha": sha, "algorithmic_bytes": {k: v[1] for k, v in parts.items()}}
     med = {}
     if trace:
         rows = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
@@ -368,11 +353,10 @@ def profile_summary_norm(d: str, workload: int) -> None:
                                                        % name.replace("'", "''")))
             m = durs[len(durs) // 2] / 1e3
             lines.append(f"  {name[:70]:70s} {n:5d} {avg / 1e3:9.2f} {m:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}")
-            for k in NORM_KERNELS:
-                if k in name:
-                    med[k] = m
+            for part, (keys, _) in parts.items():
+                if any(k in name for k in keys):
+                    med[part] = med.get(part, 0.0) + m
         lines.append("")
-    nbytes = nw.N * nw.H * nw.elem_bytes
     for tag, db, counter in (("read", fetch, "FETCH_SIZE"), ("write", write, "WRITE_SIZE")):
         if not db:
             continue
@@ -383,37 +367,85 @@ def profile_summary_norm(d: str, workload: int) -> None:
         for name, val, n in rows:
             lines.append(f"  {name[:70]:70s} {val:14.1f}  ({n} dispatches)")
         if calib:
-            factor = (nbytes / 1024.0) / calib[0][1]
+            factor = (calib_bytes / 1024.0) / calib[0][1]
             rec[f"{tag}_factor"] = factor
-            for part, keys in (("forward", ("rms_fwd",)), ("backward", ("rms_bwd", "rms_dw_reduce"))):
+            for part, (keys, _) in parts.items():
                 kib = sum(r[1] for r in rows if any(k in r[0] for k in keys))
                 rec[f"{part}_{tag}_bytes"] = kib * 1024.0 * factor
                 lines.append(f"  {part}: {kib:.1f} KiB x {factor:.4f} = {kib * 1024 * factor / 1e6:.2f} MB")
-            lines.append(f"  calibration: copy of {nbytes} B reads as {calib[0][1]:.1f} KiB -> factor {factor:.4f}")
+            lines.append(f"  calibration: copy of {calib_bytes} B reads as {calib[0][1]:.1f} KiB -> factor {factor:.4f}")
         lines.append("")
-    for part in ("forward", "backward"):
+    for part, (keys, ab) in parts.items():
         if f"{part}_read_bytes" in rec and f"{part}_write_bytes" in rec:
             t = rec[f"{part}_read_bytes"] + rec[f"{part}_write_bytes"]
             rec[f"{part}_traffic_bytes"] = t
-            lines.append(f"HBM traffic, {part} call: {t / 1e6:.2f} MB (algorithmic {ab[part] / 1e6:.2f} MB, "
-                         f"ratio {t / ab[part]:.3f})")
-    if "rms_bwd" in med:
-        bw_us = med["rms_bwd"] + med.get("rms_dw_reduce", 0.0)
-        rec["backward_us"] = bw_us
-        lines.append(f"backward call: rms_bwd {med['rms_bwd']:.2f} + rms_dw_reduce {med.get('rms_dw_reduce', 0):.2f} us"
-                     f" -> {ab['backward'] / (bw_us * 1e-6) / 1e9:.0f} GB/s algorithmic "
-                     f"({ab['backward'] / (bw_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f} GB/s)")
-    if "rms_fwd" in med:
-        rec["forward_us"] = med["rms_fwd"]
-        lines.append(f"forward call: rms_fwd {med['rms_fwd']:.2f} us -> "
-                     f"{ab['forward'] / (med['rms_fwd'] * 1e-6) / 1e9:.0f} GB/s algorithmic")
+            lines.append(f"HBM traffic, {part} call: {t / 1e6:.2f} MB (algorithmic {ab / 1e6:.2f} MB, "
+                         f"ratio {t / ab:.3f})")
+    for part, (keys, ab) in parts.items():
+        if part in med:
+            rec[f"{part}_us"] = med[part]
+            lines.append(f"{part} call ({' + '.join(keys)}): {med[part]:.2f} us (kernel medians) -> "
+                         f"{ab / (med[part] * 1e-6) / 1e9:.0f} GB/s algorithmic "
+                         f"({ab / (med[part] * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f} GB/s)")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"rmsnorm_{nw.name}.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{stem}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     if fetch or write:
-        with open(os.path.join(ROOT, "profiles", f"rmsnorm_{nw.name}.counters.json"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", f"{stem}.counters.json"), "w") as f:
             json.dump(rec, f, indent=1)
     print("\n".join(lines))
+    return rec
+
+
+def _profile_header(title: str, shape: str, sha: str, op: str, workload: int) -> list:
+    return [f"# rocprofv3 summary: {title}", f"# {shape}; kernel sources sha {sha}",
+            "# commands (from the repository root):",
+            "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
+            f"python bench.py --op {op} --workload {workload} --steps 10 --no-cpu-baseline",
+            "#   rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- "
+            f"python bench.py --op {op} --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
+            "#   rocprofv3 --pmc WRITE_SIZE -d D -o write -- "
+            f"python bench.py --op {op} --workload {workload} --steps 5 --no-cpu-baseline --calibrate",
+            f"#   python bench.py --op {op} --profile-summary D --workload {workload}", ""]
+
+
+def profile_summary_norm(d: str, workload: int) -> None:
+    """Summary of bench.py --op rmsnorm runs -> profiles/rmsnorm_<workload>.*
+    (roofline.traffic: the backward call, rms_bwd* + rms_dw_reduce)."""
+    import workloads as wl
+    workload = workload if workload in wl.NORM_WORKLOADS else 1
+    nw = wl.NORM_WORKLOADS[workload]
+    ab = norm_bytes(nw)
+    sha = kernel_sha(NORM_SOURCES)
+    head = _profile_header(f"RMSNorm forward and backward, workload {nw.name}",
+                           f"N={nw.N} H={nw.H} dtype={nw.dtype} eps={nw.eps}", sha, "rmsnorm", workload)
+    _summarize(d, f"rmsnorm_{nw.name}", head,
+               {"forward": (("rms_fwd",), ab["forward"]), "backward": (("rms_bwd", "rms_dw_reduce"), ab["backward"])},
+               nw.N * nw.H * nw.elem_bytes, sha)
+
+
+ROPE_SOURCES = ["cross_entropy_loss_amd/csrc/rope.hip", "cross_entropy_loss_amd/csrc/ce_buffer.h",
+                "cross_entropy_loss_amd/csrc/row_formats.h"]
+
+
+def rope_bytes(rw) -> int:
+    """Algorithmic HBM bytes of one ce_rope call over q and k: every element
+    read once and written once, plus the positions."""
+    return 2 * rw.T * (rw.Hq + rw.Hk) * rw.D * rw.elem_bytes + 8 * rw.T
+
+
+def profile_summary_rope(d: str, workload: int) -> None:
+    """Summary of bench.py --op rope runs -> profiles/rope_<workload>.*"""
+    import workloads as wl
+    workload = workload if workload in wl.ROPE_WORKLOADS else 1
+    rw = wl.ROPE_WORKLOADS[workload]
+    sha = kernel_sha(ROPE_SOURCES)
+    head = _profile_header(f"rotary embedding (ce_rope, forward and inverse), workload {rw.name}",
+                           f"T={rw.T} Hq={rw.Hq} Hk={rw.Hk} D={rw.D} dtype={rw.dtype} base={rw.base}", sha, "rope",
+                           workload)
+    # both launches of a step run the same kernel: per-launch figures
+    _summarize(d, f"rope_{rw.name}", head, {"launch": (("rope16", "rope32"), rope_bytes(rw))},
+               rw.T * rw.Hq * rw.D * rw.elem_bytes, sha)
 
 
 def _calib_copy_gbs(src, dst, nbytes, flush, stream, reps):
@@ -525,6 +557,97 @@ def bench_rmsnorm(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+def bench_rope(args) -> None:
+    """Rotary embedding (ce_rope) of one attention layer's q and k at packed
+    position ids: one step = the forward call and the inverse (backward) call,
+    inputs resident in HBM, L2 and MALL flushed before each call.  Roofline:
+    one launch (both are the same kernel) against HBM peak."""
+    import torch
+    import cross_entropy_loss_amd as ce
+    import workloads as wl
+    workload = args.workload if args.workload in wl.ROPE_WORKLOADS else 1
+    rw = wl.ROPE_WORKLOADS[workload]
+    q, k, pos = wl.rope_inputs(rw)
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[rw.dtype]
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16) if rw.elem_bytes == 2 else a.view(np.int32)).to(dev).view(tdt)
+
+    qd, kd, pd = to_dev(q), to_dev(k), torch.from_numpy(pos).to(dev)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        flush.fill_(2 * i)
+        if ev:
+            ev[0].record(stream)
+        qo, ko = ce.ce_rope(qd, kd, pd, rw.base)
+        if ev:
+            ev[1].record(stream)
+        flush.fill_(2 * i + 1)
+        if ev:
+            ev[2].record(stream)
+        ce.ce_rope(qo, ko, pd, rw.base, inverse=True)
+        if ev:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    copy_gbs = _calib_copy_gbs(qd, torch.empty_like(qd), qd.numel() * qd.element_size(), flush, stream,
+                               3 if args.calibrate else 7)
+    ab = rope_bytes(rw)
+    step_ms = float(fwd.mean() + bwd.mean())
+    per_launch_ms = step_ms / 2
+    gbs = ab / (per_launch_ms * 1e-3) / 1e9
+    traffic = None
+    p = os.path.join(ROOT, "profiles", f"rope_{rw.name}.counters.json")
+    if os.path.exists(p):
+        with open(p) as f:
+            c = json.load(f)
+        if c.get("kernel_sha") == kernel_sha(ROPE_SOURCES):
+            traffic = c.get("launch_traffic_bytes")
+    rec = {
+        "metric": f"RoPE fwd+bwd tokens/s and HBM GB/s (% of peak), T={rw.T} q {rw.Hq}x{rw.D} k {rw.Hk}x{rw.D} "
+                  f"{rw.dtype}",
+        "value": rw.T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": rw.dtype, "data": "synthetic",
+        "config": {"workload": rw.name, "tokens": rw.T, "q_heads": rw.Hq, "k_heads": rw.Hk, "head_dim": rw.D,
+                   "base": rw.base, "sequences": int((pos == 0).sum()), "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "rope16 (one launch: q and k)", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "copy_ceiling": copy_gbs,
+                     "frac_of_copy": gbs / copy_gbs},
+        "timing": {"forward_ms_mean": float(fwd.mean()), "forward_ms_median": float(np.median(fwd)),
+                   "inverse_ms_mean": float(bwd.mean()), "inverse_ms_median": float(np.median(bwd)),
+                   "algorithmic_bytes_per_launch": ab, "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
+                   "kernel_sha": kernel_sha(ROPE_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rope as orope
+        n, done, t0 = 128, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 8.0:
+            yq = orope.rope(q[:n], rw.dtype, pos[:n], rw.base)["y"]
+            yk = orope.rope(k[:n], rw.dtype, pos[:n], rw.base)["y"]
+            orope.rope(yq, rw.dtype, pos[:n], rw.base, inverse=True)
+            orope.rope(yk, rw.dtype, pos[:n], rw.base, inverse=True)
+            done += n
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} tokens of {rw.name}, float64 forward + inverse of q and k "
+                                         f"(numpy, one thread), {done // n} passes, {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,9 +657,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR")
-    ap.add_argument("--op", choices=["ce", "linear", "rmsnorm"], default="ce",
+    ap.add_argument("--op", choices=["ce", "linear", "rmsnorm", "rope"], default="ce",
                     help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy; "
-                         "rmsnorm: RMS layer normalisation forward + backward")
+                         "rmsnorm: RMS layer normalisation forward + backward; rope: rotary embedding of q and k")
     ap.add_argument("--chunk-rows", type=int, default=None, help="--op linear: rows per chunk")
     args = ap.parse_args()
     if args.profile_summary:
@@ -544,6 +667,8 @@ def main():
             profile_summary_linear(args.profile_summary, args.workload)
         elif args.op == "rmsnorm":
             profile_summary_norm(args.profile_summary, args.workload)
+        elif args.op == "rope":
+            profile_summary_rope(args.profile_summary, args.workload)
         else:
             profile_summary(args.profile_summary, args.workload)
         return
@@ -556,6 +681,9 @@ def main():
         return
     if args.op == "rmsnorm":
         bench_rmsnorm(args)
+        return
+    if args.op == "rope":
+        bench_rope(args)
         return
 
     import torch
