@@ -51,7 +51,8 @@ constexpr int kWaves = 4;          // forward: waves (rows in flight) per workgr
 constexpr int kBwdWaves = RMS_BWD_WAVES;       // backward: waves per workgroup (one per row in flight)
 constexpr int kMaxBwdGroups = RMS_BWD_GROUPS;  // backward workgroups: partial rows of dw
 constexpr int kMaxVPL = 32;     // forward: rows up to 32 KB (16384 bf16 / 8192 fp32)
-constexpr int kMaxBwdVPL = 8;   // backward: the per-lane dw sums (8 VPL floats) stay in VGPRs
+constexpr int kMaxBwdVPL = 8;   // backward: vectors per wave (the per-lane dw sums, 8 VPL floats, stay in
+                                // VGPRs); wider rows are split over 2 or 4 waves
 constexpr int kNT = 2;          // buffer instruction aux bits: nontemporal (streamed rows)
 
 // Waves per SIMD the register budget must allow (without a bound the
@@ -228,88 +229,117 @@ __global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd32
 template <int VPL, int EPV>
 constexpr size_t bwd_lds_floats() { return (size_t)VPL * 64 * EPV; }
 
-template <int EPV, int VPL>
+template <int EPV, int VPL, int R>
 __device__ __forceinline__ void merge_store(float (&acc)[VPL][EPV], float* la, int nvec, float* partial_row,
-                                            int lane, int wid) {
+                                            int lane, int rgi, int q) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  constexpr int Q = EPV / 4;
+  constexpr int Q = EPV / 4, RG = kBwdWaves / R;
   f4* l4 = (f4*)la;
-  for (int wv = 0; wv < kBwdWaves - 1; ++wv) {
-    if (wid == wv) {
+  for (int step = 0; step < RG - 1; ++step) {
+    if (rgi == step) {
       f4 t[VPL][Q];
 #pragma unroll
       for (int k = 0; k < VPL; ++k)
 #pragma unroll
-        for (int q = 0; q < Q; ++q) t[k][q] = wv == 0 ? f4{0.f, 0.f, 0.f, 0.f} : l4[(k * Q + q) * 64 + lane];
+        for (int u = 0; u < Q; ++u)
+          t[k][u] = step == 0 ? f4{0.f, 0.f, 0.f, 0.f} : l4[((q * VPL + k) * Q + u) * 64 + lane];
 #pragma unroll
       for (int k = 0; k < VPL; ++k)
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-          const f4 a = {acc[k][4 * q], acc[k][4 * q + 1], acc[k][4 * q + 2], acc[k][4 * q + 3]};
-          l4[(k * Q + q) * 64 + lane] = t[k][q] + a;
+        for (int u = 0; u < Q; ++u) {
+          const f4 a = {acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
+          l4[((q * VPL + k) * Q + u) * 64 + lane] = t[k][u] + a;
         }
     }
     __syncthreads();
   }
-  if (wid == kBwdWaves - 1) {
+  if (rgi == RG - 1) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int i = k * 64 + lane;
+      const int i = (q * VPL + k) * 64 + lane;
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const f4 a = {acc[k][4 * q], acc[k][4 * q + 1], acc[k][4 * q + 2], acc[k][4 * q + 3]};
-        const f4 tot = kBwdWaves > 1 ? l4[(k * Q + q) * 64 + lane] + a : a;
-        if (i < nvec) *(f4*)(partial_row + (size_t)i * EPV + 4 * q) = tot;
+      for (int u = 0; u < Q; ++u) {
+        const f4 a = {acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
+        const f4 tot = RG > 1 ? l4[((q * VPL + k) * Q + u) * 64 + lane] + a : a;
+        if (i < nvec) *(f4*)(partial_row + (size_t)i * EPV + 4 * u) = tot;
       }
     }
   }
 }
 
-template <typename T, int VPL>
+// The row's dot product from the partial sums of its R waves, in wave order
+// (R > 1: through LDS, one barrier per row; the slot alternates with the
+// iteration so a wave still reading the last row's sums is never overwritten).
+template <int R>
+__device__ __forceinline__ float group_sum(float part, float (&dp)[2][kBwdWaves], int it, int rgi, int q, int lane) {
+  if constexpr (R == 1) {
+    return part;
+  } else {
+    if (lane == 0) dp[it & 1][rgi * R + q] = part;
+    __syncthreads();
+    float s = dp[it & 1][rgi * R];
+#pragma unroll
+    for (int u = 1; u < R; ++u) s += dp[it & 1][rgi * R + u];
+    return s;
+  }
+}
+
+template <typename T, int VPL, int R>
 __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd16(
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
-  __shared__ float lds_acc[bwd_lds_floats<VPL, 8>()];
+  constexpr int RG = kBwdWaves / R;  // rows in flight per workgroup
+  __shared__ float lds_acc[bwd_lds_floats<VPL * R, 8>()];
+  __shared__ u32x4 lw[VPL * R * 64];
+  __shared__ float dp[2][kBwdWaves];
   const int lane = threadIdx.x & 63, wid = wave_id();
+  const int rgi = wid / R, q = wid % R;  // row group, and this wave's share of the row
   const int nvec = H / 8;
   const uint32_t rb = (uint32_t)H * 2, voff = (uint32_t)lane * 16;
-  __shared__ u32x4 lw[VPL * 64];
-  stage_weight<VPL>(w, nvec, lw);
+  const int sb = q * VPL * 1024;  // byte offset of this wave's columns
+  stage_weight<VPL * R>(w, nvec, lw);
+  const u32x4* lwq = lw + q * VPL * 64;
   float acc[VPL][8];
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.0f;
-  for (int64_t row = (int64_t)blockIdx.x * kBwdWaves + wid; row < N; row += (int64_t)gridDim.x * kBwdWaves) {
-    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 2, rb), rx = rsrc(x + row * ldx * 2, rb);
+  // the same trip count for every wave of the workgroup (R > 1 has a barrier
+  // per row); a row past the end has empty buffer resources: loads give 0 and
+  // stores are dropped
+  int it = 0;
+  for (int64_t r0 = (int64_t)blockIdx.x * RG; r0 < N; r0 += (int64_t)gridDim.x * RG, ++it) {
+    const int64_t row = r0 + rgi;
+    const uint32_t nb = row < N ? rb : 0u;
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 2, nb), rx = rsrc(x + row * ldx * 2, nb);
     u32x4 g[VPL], xv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      g[k] = ld_vec(rg, voff, k);
-      xv[k] = ld_vec(rx, voff, k);
+      g[k] = ld_vec(rg, voff, sb / 1024 + k);
+      xv[k] = ld_vec(rx, voff, sb / 1024 + k);
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float r = rstd[row];
+    const float r = row < N ? rstd[row] : 0.0f;
     float dot = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const u32x4 wv = lw[k * 64 + lane];
+      const u32x4 wv = lwq[k * 64 + lane];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         dot = __builtin_fmaf(T::lo(xv[k][d]) * r, T::lo(wv[d]) * T::lo(g[k][d]), dot);
         dot = __builtin_fmaf(T::hi(xv[k][d]) * r, T::hi(wv[d]) * T::hi(g[k][d]), dot);
       }
     }
-    const float c = wave_sum(dot) / (float)H;
+    const float c = group_sum<R>(wave_sum(dot), dp, it, rgi, q, lane) / (float)H;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       fence_regs(g[k]);
       fence_regs(xv[k]);
     }
-    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 2, rb);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 2, nb);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const u32x4 wv = lw[k * 64 + lane];
+      const u32x4 wv = lwq[k * 64 + lane];
       u32x4 o;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -319,56 +349,72 @@ __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bw
         acc[k][2 * d] = __builtin_fmaf(gl, xl, acc[k][2 * d]);
         acc[k][2 * d + 1] = __builtin_fmaf(gh, xh, acc[k][2 * d + 1]);
       }
-      buf_store<kNT>(o, ro, voff, k * 1024);
+      buf_store<kNT>(o, ro, voff, sb + k * 1024);
     }
   }
-  merge_store(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, wid);
+  merge_store<8, VPL, R>(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, rgi, q);
 }
 
 // Backward, fp32 rows: y-side arithmetic in fp64, the dw sums in fp32.
-template <int VPL>
+template <int VPL, int R>
 __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd32(
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
-  __shared__ float lds_acc[bwd_lds_floats<VPL, 4>()];
+  constexpr int RG = kBwdWaves / R;
+  __shared__ float lds_acc[bwd_lds_floats<VPL * R, 4>()];
+  __shared__ u32x4 lw[VPL * R * 64];
+  __shared__ double dpd[2][kBwdWaves];
   const int lane = threadIdx.x & 63, wid = wave_id();
+  const int rgi = wid / R, q = wid % R;
   const int nvec = H / 4;
   const uint32_t rb = (uint32_t)H * 4, voff = (uint32_t)lane * 16;
-  __shared__ u32x4 lw[VPL * 64];
-  stage_weight<VPL>(w, nvec, lw);
+  const int sb = q * VPL * 1024;
+  stage_weight<VPL * R>(w, nvec, lw);
+  const u32x4* lwq = lw + q * VPL * 64;
   float acc[VPL][4];
 #pragma unroll
   for (int k = 0; k < VPL; ++k)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[k][e] = 0.0f;
-  for (int64_t row = (int64_t)blockIdx.x * kBwdWaves + wid; row < N; row += (int64_t)gridDim.x * kBwdWaves) {
-    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 4, rb), rx = rsrc(x + row * ldx * 4, rb);
+  int it = 0;
+  for (int64_t r0 = (int64_t)blockIdx.x * RG; r0 < N; r0 += (int64_t)gridDim.x * RG, ++it) {
+    const int64_t row = r0 + rgi;
+    const uint32_t nb = row < N ? rb : 0u;
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dy + row * lddy * 4, nb), rx = rsrc(x + row * ldx * 4, nb);
     u32x4 g[VPL], xv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      g[k] = ld_vec(rg, voff, k);
-      xv[k] = ld_vec(rx, voff, k);
+      g[k] = ld_vec(rg, voff, sb / 1024 + k);
+      xv[k] = ld_vec(rx, voff, sb / 1024 + k);
     }
     __builtin_amdgcn_sched_barrier(0);
-    const double r = (double)rstd[row];
+    const double r = row < N ? (double)rstd[row] : 0.0;
     double dot = 0.0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const u32x4 wv = lw[k * 64 + lane];
+      const u32x4 wv = lwq[k * 64 + lane];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         dot = fma((double)as_f(xv[k][d]) * r, (double)as_f(wv[d]) * (double)as_f(g[k][d]), dot);
     }
-    const double c = wave_sum(dot) / (double)H;
+    dot = wave_sum(dot);
+    if constexpr (R > 1) {  // the row's R partial sums, in wave order
+      if (lane == 0) dpd[it & 1][rgi * R + q] = dot;
+      __syncthreads();
+      dot = dpd[it & 1][rgi * R];
+#pragma unroll
+      for (int u = 1; u < R; ++u) dot += dpd[it & 1][rgi * R + u];
+    }
+    const double c = dot / (double)H;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       fence_regs(g[k]);
       fence_regs(xv[k]);
     }
-    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 4, rb);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(dx + row * lddx * 4, nb);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const u32x4 wv = lw[k * 64 + lane];
+      const u32x4 wv = lwq[k * 64 + lane];
       u32x4 o;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -376,10 +422,10 @@ __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bw
         o[d] = __builtin_bit_cast(uint32_t, (float)(r * ((double)as_f(wv[d]) * gd - xh * c)));
         acc[k][d] = __builtin_fmaf((float)gd, (float)xh, acc[k][d]);
       }
-      buf_store<kNT>(o, ro, voff, k * 1024);
+      buf_store<kNT>(o, ro, voff, sb + k * 1024);
     }
   }
-  merge_store(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, wid);
+  merge_store<4, VPL, R>(acc, lds_acc, nvec, partial + (int64_t)blockIdx.x * H, lane, rgi, q);
 }
 
 // dw[j] = sum over the G partial rows in fp64, rounded once.  A workgroup
@@ -456,7 +502,8 @@ typedef void (*BwdFn)(const char*, int64_t, const char*, int64_t, const char*, c
                       int64_t, float*);
 
 #define RMS_VPL_CASES(MAKE) MAKE(1) MAKE(2) MAKE(4) MAKE(8) MAKE(16) MAKE(32)
-#define RMS_BWD_VPL_CASES(MAKE) MAKE(1) MAKE(2) MAKE(4) MAKE(8)
+// backward: total vectors per lane -> (vectors per wave, waves per row)
+#define RMS_BWD_CASES(MAKE) MAKE(1, 1) MAKE(2, 1) MAKE(4, 1) MAKE(8, 1) MAKE(8, 2) MAKE(8, 4)
 
 FwdFn fwd_fn(int dtype, int vpl) {
 #define MAKE(V)                                          \
@@ -470,13 +517,14 @@ FwdFn fwd_fn(int dtype, int vpl) {
   return nullptr;
 }
 BwdFn bwd_fn(int dtype, int vpl) {
-#define MAKE(V)                                          \
-  if (vpl == V) {                                        \
-    if (dtype == CE_DTYPE_BF16) return rms_bwd16<BF16, V>; \
-    if (dtype == CE_DTYPE_F16) return rms_bwd16<F16, V>;   \
-    return rms_bwd32<V>;                                 \
+  const int r = vpl > kMaxBwdVPL ? vpl / kMaxBwdVPL : 1, v = vpl / r;
+#define MAKE(V, R)                                             \
+  if (v == V && r == R) {                                      \
+    if (dtype == CE_DTYPE_BF16) return rms_bwd16<BF16, V, R>;  \
+    if (dtype == CE_DTYPE_F16) return rms_bwd16<F16, V, R>;    \
+    return rms_bwd32<V, R>;                                    \
   }
-  RMS_BWD_VPL_CASES(MAKE)
+  RMS_BWD_CASES(MAKE)
 #undef MAKE
   return nullptr;
 }
@@ -521,7 +569,7 @@ int ce_rmsnorm_backward(const void* dy, int64_t ld_dy, const void* x, int64_t ld
   if (dweight == nullptr || weight == nullptr) return CE_ERR_INVALID_ARG;
   if (N > 0 && (dy == nullptr || x == nullptr || rstd == nullptr || dx == nullptr)) return CE_ERR_INVALID_ARG;
   const int es = esize(dtype), vpl = vpl_for(H, dtype);
-  if (vpl == 0 || vpl > kMaxBwdVPL) return CE_ERR_UNSUPPORTED;
+  if (vpl == 0 || bwd_fn(dtype, vpl) == nullptr) return CE_ERR_UNSUPPORTED;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(weight) || !aligned16(dx) || (ld_dy * es) % 16 ||
       (ld_x * es) % 16 || (ld_dx * es) % 16)
     return CE_ERR_UNSUPPORTED;

@@ -230,7 +230,7 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
  * 16-bit sum of squares runs in fp32 and is redone in fp64 when it overflows
  * or falls below 2^-100; with eps = 0, a row whose root mean square is below
  * 2^-128 gives rstd = inf.
- * Backward: hidden up to 4096 (16-bit) / 2048 (fp32); dx may be dy itself
+ * Backward: hidden up to 16384 (16-bit) / 8192 (fp32); dx may be dy itself
  * (same stride); dweight is summed over the rows in fixed order
  * (deterministic) through a workspace of ce_rmsnorm_workspace_bytes() bytes
  * (256-byte aligned, no preparation needed, contents overwritten: not a

@@ -256,8 +256,8 @@ def test_rmsnorm_forward_rejects(lib, kw, code):
     (dict(dx=0), _lib.CE_ERR_INVALID_ARG),
     (dict(dw=FAKE + 1), _lib.CE_ERR_INVALID_ARG),
     (dict(dx=FAKE, lddx=72), _lib.CE_ERR_INVALID_ARG),  # in place with another stride
-    (dict(H=4104, lddy=4104, ldx=4104, lddx=4104), _lib.CE_ERR_UNSUPPORTED),
-    (dict(dtype=0, H=2052, lddy=2052, ldx=2052, lddx=2052), _lib.CE_ERR_UNSUPPORTED),
+    (dict(H=16392, lddy=16392, ldx=16392, lddx=16392), _lib.CE_ERR_UNSUPPORTED),
+    (dict(dtype=0, H=8196, lddy=8196, ldx=8196, lddx=8196), _lib.CE_ERR_UNSUPPORTED),
     (dict(H=12, lddy=12, ldx=12, lddx=12), _lib.CE_ERR_UNSUPPORTED),
     (dict(x=FAKE + 8), _lib.CE_ERR_UNSUPPORTED),
     (dict(ws=0), _lib.CE_ERR_WORKSPACE),

@@ -148,8 +148,11 @@ def test_rmsnorm_forward_parity(dtype, N, H, ld):
     check_forward(y, rstd, x, w, dtype, eps)
 
 
+# rows split over 2 or 4 waves past 4096 (16-bit) / 2048 (fp32) elements: 4104, 8192, 12296, 16384; 4096, 8192
 BWD_CASES = [("bf16", 37, 8), ("bf16", 64, 512), ("bf16", 1031, 4096), ("f16", 700, 4096), ("f32", 301, 2048),
-             ("bf16", 5, 2056), ("f16", 2000, 1000), ("f32", 64, 252), ("bf16", 3, 64)]
+             ("bf16", 5, 2056), ("f16", 2000, 1000), ("f32", 64, 252), ("bf16", 3, 64),
+             ("bf16", 37, 4104), ("bf16", 515, 8192), ("f16", 21, 12296), ("bf16", 130, 16384), ("f32", 77, 4096),
+             ("f32", 9, 8192), ("bf16", 2500, 8192)]
 
 
 @pytest.mark.parametrize("dtype,N,H", BWD_CASES, ids=[f"{d}-N{n}-H{h}" for d, n, h in BWD_CASES])
