@@ -18,7 +18,8 @@
 //   3. g rounded to the input format (bf16 / fp16) for the two GEMMs below
 //   4. dh_c = g W                    rocBLAS GEMM, fp32 accumulate, dtype out
 //   5. dW32 += g^T h_c               rocBLAS GEMM, fp32 accumulate and out
-// then dW32 is rounded once to the input format, and the token mean over the
+// then dW32 is rounded once to the input format (with a single chunk the GEMM
+// writes the input format itself, from its fp32 sums), and the token mean over the
 // whole batch is summed in row order in fp64.  The batch's logits are never
 // stored: one fp32 chunk (T x V) lives in the workspace.
 //
@@ -85,8 +86,10 @@ LinLayout lin_layout(int64_t N, int64_t H, int64_t V, int64_t chunk_rows, int dt
   if (dtype != CE_DTYPE_F32) {
     L.g16 = off;
     off += align256((size_t)Tc * V * 2);
-    L.dw32 = off;
-    off += align256((size_t)V * H * 4);
+    if (L.nc > 1) {  // one chunk: the weight-gradient GEMM writes the output format directly
+      L.dw32 = off;
+      off += align256((size_t)V * H * 4);
+    }
   }
   const size_t nc = (size_t)(L.nc > 0 ? L.nc : 1);
   L.dl_chunk = off;
@@ -307,8 +310,12 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
   float* chunk_loss = (float*)(ws + L.chunk_loss);
   int32_t* chunk_n = (int32_t*)(ws + L.chunk_n);
   void* g_lo = (dtype == CE_DTYPE_F32) ? (void*)logits : (void*)(ws + L.g16);
-  float* dw32 = (dtype == CE_DTYPE_F32) ? (float*)grad_weight : (float*)(ws + L.dw32);
-  const int64_t ld_dw = (dtype == CE_DTYPE_F32) ? ld_grad_weight : H;
+  // the weight gradient: accumulated over chunks in fp32 (the output itself for
+  // fp32, else a workspace copy rounded once at the end); a single chunk is
+  // written by its GEMM in the output format (fp32 accumulation, one rounding)
+  const bool dw_direct = dtype == CE_DTYPE_F32 || L.nc == 1;
+  float* dw32 = dw_direct ? (float*)grad_weight : (float*)(ws + L.dw32);
+  const int64_t ld_dw = dw_direct ? ld_grad_weight : H;
   const rocblas_datatype dt = blas_type(dtype);
   const float* one = (const float*)(ws + L.consts);
   const float* zero = one + 1;
@@ -381,13 +388,18 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
     }
     // 5. dW [V x H] += g^T h_c  (column-major: H x V = (H x Tc)(Tc x V))
     if (grad_weight) {
-      rc = gemm(bh, rocblas_operation_none, rocblas_operation_transpose, H, V, Tc, one, hc, dt, ld_hidden, g_lo, dt,
-                V, c == 0 ? zero : one, dw32, rocblas_datatype_f32_r, ld_dw);
+      if (dw_direct)  // fp32: accumulate in the output; one 16-bit chunk: scale by 2^-k and round once
+        rc = gemm(bh, rocblas_operation_none, rocblas_operation_transpose, H, V, Tc,
+                  dtype == CE_DTYPE_F32 ? one : down, hc, dt, ld_hidden, g_lo, dt, V, c == 0 ? zero : one, dw32,
+                  dtype == CE_DTYPE_F32 ? rocblas_datatype_f32_r : dt, ld_dw);
+      else
+        rc = gemm(bh, rocblas_operation_none, rocblas_operation_transpose, H, V, Tc, one, hc, dt, ld_hidden, g_lo, dt,
+                  V, c == 0 ? zero : one, dw32, rocblas_datatype_f32_r, ld_dw);
       if (rc != CE_OK) break;
     }
   }
   if (rc != CE_OK) return rc;
-  if (grad_weight && dtype != CE_DTYPE_F32) {
+  if (grad_weight && !dw_direct) {
     if (dtype == CE_DTYPE_BF16)
       hipLaunchKernelGGL(lin_cast_kernel<__bf16>, dim3((unsigned)V), dim3(256), 0, st, dw32, H, H,
                          (__bf16*)grad_weight, ld_grad_weight, down);
