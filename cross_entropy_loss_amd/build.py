@@ -14,7 +14,7 @@ SRC = os.path.join(HERE, "csrc", "ce_api.hip")
 SRCS = [SRC] + [os.path.join(HERE, "csrc", f) for f in ("ce_linear.hip", "rmsnorm.hip", "rope.hip")]
 HEADERS = ("ce_kernels.h", "ce_buffer.h", "ce_internal.h", "row_formats.h")
 DEPS = SRCS + [os.path.join(HERE, "csrc", h) for h in HEADERS] + [os.path.join(ROOT, "include", "ce_mi355x.h")]
-LIBS = ["-lrocblas"]  # the LM-head entry point's GEMMs
+LIBS = ["-lrocblas", "-lhipblaslt"]  # the LM-head entry point's GEMMs
 LIB = os.path.join(HERE, "libce_mi355x.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib_copy.hip")
 CALIB_LIB = os.path.join(HERE, "libce_calib.so")

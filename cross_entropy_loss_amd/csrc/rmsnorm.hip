@@ -59,8 +59,8 @@ constexpr int kNT = 2;          // buffer instruction aux bits: nontemporal (str
 // compiler has taken up to 256 VGPRs for these shapes, one wave per SIMD).
 template <int VPL>
 constexpr int fwd_min_waves() { return VPL <= 4 ? 8 : (VPL <= 8 ? 6 : (VPL <= 16 ? 4 : 2)); }
-template <int VPL>
-constexpr int bwd_min_waves() { return VPL <= 4 ? 4 : 3; }
+template <int VPL, int R = 1>
+constexpr int bwd_min_waves() { return R >= 4 ? 2 : (VPL <= 4 ? 4 : 3); }  // R = 4: LDS allows 2 per SIMD
 
 // Makes the compiler treat v as redefined here, so that values it derived
 // from v earlier (unpacked floats) are recomputed rather than kept live
@@ -285,7 +285,7 @@ __device__ __forceinline__ float group_sum(float part, float (&dp)[2][kBwdWaves]
 }
 
 template <typename T, int VPL, int R>
-__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd16(
+__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL, R>())) void rms_bwd16(
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
   constexpr int RG = kBwdWaves / R;  // rows in flight per workgroup
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bw
 
 // Backward, fp32 rows: y-side arithmetic in fp64, the dw sums in fp32.
 template <int VPL, int R>
-__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL>())) void rms_bwd32(
+__global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL, R>())) void rms_bwd32(
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
   constexpr int RG = kBwdWaves / R;

@@ -192,9 +192,14 @@ int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t 
  *                 workspace of a chunk, a chunk of fp32 logits and, for
  *                 bf16/fp16, the chunk's rounded gradient and the fp32
  *                 grad_weight accumulator (vocab x hidden_size x 4 bytes).
- * Memory: apart from the workspace, rocBLAS keeps one handle per device for the
- * process lifetime (with the memory it allocates for itself); calls on one
- * device are serialised on the host around that handle.
+ * GEMMs: hipBLASLt for bf16 / fp16 (its first heuristic algorithm among those
+ * needing no workspace), rocBLAS for fp32 and for shapes hipBLASLt has no
+ * algorithm for; both accumulate in fp32 without atomics (repeated calls give
+ * identical results).
+ * Memory: apart from the workspace, rocBLAS and hipBLASLt keep one handle per
+ * device for the process lifetime (with the memory they allocate for
+ * themselves), and the GEMM descriptors chosen per shape are kept on the host;
+ * calls on one device are serialised on the host around those handles.
  * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
  * dimension of 2^31 or more give CE_ERR_UNSUPPORTED (the GEMMs take 32-bit
  * sizes); a failed GEMM gives CE_ERR_HIP.
