@@ -60,7 +60,7 @@ constexpr int kNT = 2;          // buffer instruction aux bits: nontemporal (str
 template <int VPL>
 constexpr int fwd_min_waves() { return VPL <= 4 ? 8 : (VPL <= 8 ? 6 : (VPL <= 16 ? 4 : 2)); }
 template <int VPL, int R = 1>
-constexpr int bwd_min_waves() { return R >= 4 ? 2 : (VPL <= 4 ? 4 : 3); }  // R = 4: LDS allows 2 per SIMD
+constexpr int bwd_min_waves() { return R >= 2 ? 2 : (VPL <= 4 ? 4 : 3); }  // R >= 2: LDS allows 2 per SIMD
 
 // Makes the compiler treat v as redefined here, so that values it derived
 // from v earlier (unpacked floats) are recomputed rather than kept live
@@ -218,13 +218,13 @@ __global__ __launch_bounds__(64 * kWaves, (fwd_min_waves<VPL>())) void rms_fwd32
 // LDS and written as the workgroup's partial row of dw.  Lanes past the row
 // load zeros (and a zero weight), so they add nothing to the sums.
 //
-// LDS: the weight row (static, staged once), and the running dw sums laid out
-// [vector k][quad q][lane][4] with compile-time strides, so a wave moves its
-// sums with 16-byte LDS accesses that the compiler can batch (with a runtime
-// stride it could not prove the addresses apart and waited out every
-// read-add-write in turn).  Waves 0 .. W-2 add into LDS in order; the last
-// wave adds the total to its own sums in registers and writes the partial
-// row straight to memory: ((s0 + s1) + ...) + s(W-1), a fixed order.
+// LDS: the weight row (static, staged once), and slots for the row groups' dw
+// sums laid out [slot][wave share][vector k][quad][lane][4] with compile-time
+// strides, so a wave moves its sums with 16-byte LDS accesses that the
+// compiler can batch (with a runtime stride it could not prove the addresses
+// apart and waited out every read-add-write in turn).  The row groups' sums
+// meet in a pairwise tree (log2 of the groups' count steps, a fixed order);
+// group 0 writes the workgroup's partial row straight from its registers.
 // ---------------------------------------------------------------------------
 template <int VPL, int EPV>
 constexpr size_t bwd_lds_floats() { return (size_t)VPL * 64 * EPV; }
@@ -235,34 +235,43 @@ __device__ __forceinline__ void merge_store(float (&acc)[VPL][EPV], float* la, i
   typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int Q = EPV / 4, RG = kBwdWaves / R;
   f4* l4 = (f4*)la;
-  for (int step = 0; step < RG - 1; ++step) {
-    if (rgi == step) {
-      f4 t[VPL][Q];
+  // pairwise tree over the row groups: at stride st, group rgi + st hands its
+  // sums to group rgi (rgi a multiple of 2 st) through LDS slot rgi / (2 st),
+  // which adds them to its own: ((s0 + s1) + (s2 + s3)) + ..., a fixed order
+  for (int st = 1; st < RG; st *= 2) {
+    const int slot = rgi / (2 * st);
+    if (rgi % (2 * st) == st) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k)
 #pragma unroll
         for (int u = 0; u < Q; ++u)
-          t[k][u] = step == 0 ? f4{0.f, 0.f, 0.f, 0.f} : l4[((q * VPL + k) * Q + u) * 64 + lane];
+          l4[(((slot * R + q) * VPL + k) * Q + u) * 64 + lane] =
+              f4{acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
+    }
+    __syncthreads();
+    if (rgi % (2 * st) == 0) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k)
 #pragma unroll
         for (int u = 0; u < Q; ++u) {
-          const f4 a = {acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
-          l4[((q * VPL + k) * Q + u) * 64 + lane] = t[k][u] + a;
+          const f4 b = l4[(((slot * R + q) * VPL + k) * Q + u) * 64 + lane];
+          acc[k][4 * u] += b.x;
+          acc[k][4 * u + 1] += b.y;
+          acc[k][4 * u + 2] += b.z;
+          acc[k][4 * u + 3] += b.w;
         }
     }
     __syncthreads();
   }
-  if (rgi == RG - 1) {
+  if (rgi == 0) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int i = (q * VPL + k) * 64 + lane;
 #pragma unroll
-      for (int u = 0; u < Q; ++u) {
-        const f4 a = {acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
-        const f4 tot = RG > 1 ? l4[((q * VPL + k) * Q + u) * 64 + lane] + a : a;
-        if (i < nvec) *(f4*)(partial_row + (size_t)i * EPV + 4 * u) = tot;
-      }
+      for (int u = 0; u < Q; ++u)
+        if (i < nvec)
+          *(f4*)(partial_row + (size_t)i * EPV + 4 * u) =
+              f4{acc[k][4 * u], acc[k][4 * u + 1], acc[k][4 * u + 2], acc[k][4 * u + 3]};
     }
   }
 }
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL, R>())) void rms
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
   constexpr int RG = kBwdWaves / R;  // rows in flight per workgroup
-  __shared__ float lds_acc[bwd_lds_floats<VPL * R, 8>()];
+  __shared__ float lds_acc[bwd_lds_floats<VPL * kBwdWaves / 2, 8>()];  // the tree's slots
   __shared__ u32x4 lw[VPL * R * 64];
   __shared__ float dp[2][kBwdWaves];
   const int lane = threadIdx.x & 63, wid = wave_id();
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, (bwd_min_waves<VPL, R>())) void rms
     const char* dy, int64_t lddy, const char* x, int64_t ldx, const char* w, const float* rstd, int64_t N, int H,
     char* dx, int64_t lddx, float* partial) {
   constexpr int RG = kBwdWaves / R;
-  __shared__ float lds_acc[bwd_lds_floats<VPL * R, 4>()];
+  __shared__ float lds_acc[bwd_lds_floats<VPL * kBwdWaves / 2, 4>()];
   __shared__ u32x4 lw[VPL * R * 64];
   __shared__ double dpd[2][kBwdWaves];
   const int lane = threadIdx.x & 63, wid = wave_id();
