@@ -1,7 +1,10 @@
 /*
  * ce_mi355x.h -- C ABI of the MI355X (gfx950) token-level softmax
  * cross-entropy library: forward, backward, and the fused forward+backward
- * that writes the gradient over the logits.
+ * that writes the gradient over the logits; around it, the LM-head projection
+ * fused with the loss (ce_linear_*), RMS layer normalisation (ce_rmsnorm_*)
+ * and the rotary position embedding with position ids (ce_rope), each
+ * declared below with the passage that defines it.
  *
  * The operation.  The pages name a "Fast Cross Entropy" kernel (PyPI page
  * "fms-acceleration-foak 0.7.4", kernel list) that replaces a causal LM's
@@ -25,7 +28,7 @@
  * Conventions shared by every entry point
  *   - Every pointer argument is a device pointer owned by the caller; the
  *     library allocates no memory and keeps no pointer after return (the
- *     LM-head entry point's GEMM library is the one exception, see there).
+ *     LM-head entry point's GEMM libraries are the one exception, see there).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
  *     stream).  No entry point synchronises the stream or reads device data on
  *     the host; outputs are valid once the stream work completes, and inputs
@@ -45,7 +48,8 @@
  *   - Results are deterministic: the same inputs give the same bits.
  *   - Precision: bf16/fp16 inputs are computed in fp32 and the gradient is
  *     rounded once to the input format (nearest-even, subnormals kept); fp32
- *     inputs are computed in fp64 and rounded once to fp32.
+ *     inputs are computed in fp64 and rounded once to fp32 (each entry point
+ *     below states its own arithmetic).
  */
 #ifndef CE_MI355X_H
 #define CE_MI355X_H
