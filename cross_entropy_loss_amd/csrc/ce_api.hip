@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ce_internal.h"
 #include "ce_kernels.h"
 #include "ce_mi355x.h"
@@ -97,23 +99,30 @@ int counters_for(int64_t N, int64_t G) {
   return (int)k;
 }
 
-// Co-resident workgroups of a kernel on the current device (cached per kernel).
+// Co-resident workgroups of a kernel on the current device (cached per device
+// and kernel; the cache is shared by every host thread, hence the lock).
 int64_t resident_blocks(KernelFn fn, int block) {
-  static KernelFn fns[64];
-  static int64_t vals[64];
+  struct Entry {
+    int dev;
+    KernelFn fn;
+    int block;
+    int64_t val;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
   static int n = 0;
-  for (int i = 0; i < n; ++i)
-    if (fns[i] == fn) return vals[i];
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+      if (cache[i].dev == dev && cache[i].fn == fn && cache[i].block == block) return cache[i].val;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, block, 0) != hipSuccess) return 0;
   const int64_t r = (int64_t)cus * per_cu;
-  if (n < 64) {
-    fns[n] = fn;
-    vals[n] = r;
-    ++n;
-  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (n < 64) cache[n++] = Entry{dev, fn, block, r};
   return r;
 }
 

@@ -259,7 +259,21 @@ struct LtPlan {
 hipblasLtHandle_t g_lt[kMaxDevices];
 bool g_lt_failed[kMaxDevices];
 std::vector<LtPlan> g_plans[kMaxDevices];
+// Plans kept per device; past this many (callers whose row counts keep
+// changing) the oldest is destroyed, so the cache stays bounded.
+constexpr size_t kMaxPlans = 128;
 
+void destroy_plan(LtPlan& p) {
+  if (p.md) hipblasLtMatmulDescDestroy(p.md);
+  if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+  if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+  if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
+  p.md = nullptr;
+  p.la = p.lb = p.lc = nullptr;
+}
+
+// The plan for a GEMM shape (nullptr: hipBLASLt offers none).  Called with the
+// device's lock held; the pointer is valid until the next call.
 const LtPlan* lt_plan(int dev, bool ta, bool tb, int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
                       int64_t ldc, hipDataType ab, hipDataType c) {
   if (g_lt_failed[dev]) return nullptr;
@@ -296,6 +310,11 @@ const LtPlan* lt_plan(int dev, bool ta, bool tb, int64_t m, int64_t n, int64_t k
          nres > 0 && res.workspaceSize == 0;
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
   if (p.ok) p.algo = res.algo;
+  else destroy_plan(p);  // remembered as unavailable: rocBLAS serves the shape
+  if (g_plans[dev].size() >= kMaxPlans) {
+    destroy_plan(g_plans[dev].front());
+    g_plans[dev].erase(g_plans[dev].begin());
+  }
   g_plans[dev].push_back(p);
   return p.ok ? &g_plans[dev].back() : nullptr;
 }

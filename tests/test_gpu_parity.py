@@ -288,6 +288,48 @@ def test_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
+def test_concurrent_host_threads():
+    # two host threads, each with its own stream and (through the binding)
+    # its own workspace, call the fused entry point at the same time: one on
+    # the persistent wide-row kernel, one on the row-per-workgroup kernel;
+    # every call must reproduce the single-threaded result bit for bit
+    import threading
+
+    cases = []
+    for seed, V in ((61, 128256), (62, 32000)):
+        w = wl.custom("threads", seed, 48, V, "bf16", 2.0, 0.05)
+        bits, p = wl.make(w)
+        out, g = run_fused(bits, p.labels, "bf16")
+        check_against_oracle(out, g, bits, p.labels, "bf16")
+        cases.append((bits, p.labels, to_host_bits(g, "bf16"), float(out["loss_mean"].item())))
+    errors = []
+
+    def worker(i):
+        try:
+            bits, labels, g_ref, L_ref = cases[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                y = torch.from_numpy(np.ascontiguousarray(labels)).cuda()
+                for it in range(12):
+                    x = to_device(bits, "bf16")
+                    out = ce.ce_fwd_bwd_inplace(x, y)
+                    s.synchronize()
+                    if float(out["loss_mean"].item()) != L_ref or not (to_host_bits(x, "bf16") == g_ref).all():
+                        errors.append(f"thread {i}, call {it}: result differs from the single-threaded call")
+                        return
+        except Exception as e:  # reported below, in the main thread
+            errors.append(f"thread {i}: {e!r}")
+
+    _say("[threads] bf16 48x128256 and 48x32000 on two host threads")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+
+
 @pytest.mark.parametrize("dtype,V,chunk", [("bf16", 32000, 0), ("f16", 5000, 0), ("f32", 1000, 0),
                                            ("bf16", 70000, 32768), ("f32", 3000, 1000), ("bf16", 150001, 65536),
                                            ("f32", 70001, 0)])
