@@ -214,6 +214,38 @@ __device__ __forceinline__ void ms_merge(double& m, double& s, double m2, double
   m = M;
   s = a + b;
 }
+// e^d in fp64 for the per-element passes over fp32 rows.  t = d log2(e) is
+// split as n + f with n = rint(t) and |f| <= 1/2, so e^d = 2^n e^(f ln 2); the
+// second factor is the Taylor series of the exponential at 0 in f ln 2 to
+// degree 11, whose truncation error is below 7e-15 relative for
+// |f ln 2| <= 0.35, and 2^n is applied exactly by ldexp.  The relative error is
+// a few 1e-15 wherever the result is a normal fp64 number, far inside the
+// 6e-8 that one rounding to fp32 leaves for a 1-ulp gradient.  t below -1100
+// (d = -inf included) gives +0; NaN stays NaN.  About 21 VALU instructions,
+// against about twice that for the library exp with its special-case
+// handling; the library exp and log remain in use for per-row quantities.
+constexpr double kLn2d = 0.69314718055994530942;
+constexpr double kLog2ed = 1.44269504088896340736;
+constexpr double taylor_coef(int k) {  // (ln 2)^k / k!
+  double r = 1.0;
+  for (int i = 1; i <= k; ++i) r = r * kLn2d / i;
+  return r;
+}
+__device__ __forceinline__ double exp_f64(double d) {
+  constexpr double c[12] = {taylor_coef(0), taylor_coef(1), taylor_coef(2),  taylor_coef(3),
+                            taylor_coef(4), taylor_coef(5), taylor_coef(6),  taylor_coef(7),
+                            taylor_coef(8), taylor_coef(9), taylor_coef(10), taylor_coef(11)};
+  const double t = d * kLog2ed;
+  const double n = __builtin_rint(t);
+  const double f = t - n;
+  double p = c[11];
+#pragma unroll
+  for (int k = 10; k >= 0; --k) p = fma(p, f, c[k]);
+  const int ni = (int)fmin(fmax(n, -2000.0), 2000.0);  // NaN -> -2000 (p is NaN then)
+  const double r = ldexp(p, ni);
+  return (t < -1100.0) ? 0.0 : r;
+}
+
 template <typename F>
 __device__ __forceinline__ void wave_ms(F& m, F& s) {
 #pragma unroll
@@ -1217,12 +1249,13 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
     }
     double m = (double)mf;
     const double mm = (mf == -INFINITY) ? 0.0 : m;
-    double s = exp((double)xh - mm) + exp((double)xt - mm);
+    double s4[4] = {exp_f64((double)xh - mm), exp_f64((double)xt - mm), 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
       if (k * NT + tid < g.nvec)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) s += exp((double)as<float>(v[k][d]) - mm);
+        for (int d = 0; d < 4; ++d) s4[d] += exp_f64((double)as<float>(v[k][d]) - mm);
+    double s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     wave_ms(m, s);
     if (lane == 0) {
       lds_m[wid] = m;
@@ -1246,31 +1279,30 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
       const double scale = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)n;
       char* gbase = a.grad + row * a.grad_ld * ESZ;
       u32x4* gbody = (u32x4*)(gbase + g.head * ESZ);
-      const double gy = -scale * pcomp;
-      const float nanv = __builtin_nanf("");
+      if (badlab) {
+        nan_row<F32, NT, VPL, POL>(gbase, g, tid, 0);
+      } else {
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int idx = k * NT + tid;
-        if (idx < g.nvec) {
-          u32x4 o;
+        for (int k = 0; k < VPL; ++k) {
+          const int idx = k * NT + tid;
+          if (idx < g.nvec) {
+            u32x4 o;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            double gd = exp((double)as<float>(v[k][d]) - lse) * scale;
-            if (k == own.k && d == own.e) gd = gy;
-            o[d] = __builtin_bit_cast(uint32_t, badlab ? nanv : (float)gd);
+            for (int d = 0; d < 4; ++d)
+              o[d] = __builtin_bit_cast(uint32_t, (float)(exp_f64((double)as<float>(v[k][d]) - lse) * scale));
+            stv<POL>(gbody + idx, o);
           }
-          stv<POL>(gbody + idx, o);
         }
-      }
-      if (has_h) {
-        double gh = exp((double)xh - lse) * scale;
-        if (own.head > 0) gh = gy;
-        ((float*)gbase)[tid] = badlab ? nanv : (float)gh;
-      }
-      if (has_t) {
-        double gt = exp((double)xt - lse) * scale;
-        if (own.tail > 0) gt = gy;
-        ((float*)gbase)[g.head + (int64_t)g.nvec * EPV + tid] = badlab ? nanv : (float)gt;
+        float* grow = (float*)gbase;
+        const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
+        if (has_h) grow[tid] = (float)(exp_f64((double)xh - lse) * scale);
+        if (has_t) grow[jt] = (float)(exp_f64((double)xt - lse) * scale);
+        // the label's gradient overwrites the value just stored for it (same
+        // lane, same address: program order)
+        const float gy = (float)(-scale * pcomp);
+        if (own.k >= 0) ((float*)gbody)[(int64_t)(own.k * NT + tid) * EPV + own.e] = gy;
+        if (own.head > 0) grow[tid] = gy;
+        if (own.tail > 0) grow[jt] = gy;
       }
     }
   } else {
@@ -1352,30 +1384,28 @@ __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
     for (int k = 0; k < VPL; ++k) {
       const int idx = v0 + k * NT + tid;
       if (idx < g.nvec) {
-        const int64_t j0 = g.head + (int64_t)idx * EPV;
         u32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          double gd = exp((double)as<float>(v[k][d]) - lse_d) * scale_d;
-          if (j0 + d == y) gd = gy_d;
-          o[d] = __builtin_bit_cast(uint32_t, (float)gd);
-        }
+        for (int d = 0; d < 4; ++d)
+          o[d] = __builtin_bit_cast(uint32_t, (float)(exp_f64((double)as<float>(v[k][d]) - lse_d) * scale_d));
         stv<POL>(gbody + idx, o);
       }
     }
+    float* grow = (float*)gbase;
     if (slab == 0) {
-      if (tid < g.head) {
-        double gh = exp((double)((const float*)rbase)[tid] - lse_d) * scale_d;
-        if ((int64_t)tid == y) gh = gy_d;
-        ((float*)gbase)[tid] = (float)gh;
-      }
+      if (tid < g.head) grow[tid] = (float)(exp_f64((double)((const float*)rbase)[tid] - lse_d) * scale_d);
       if (tid < g.tail) {
         const int64_t j = g.head + (int64_t)g.nvec * EPV + tid;
-        double gt = exp((double)((const float*)rbase)[j] - lse_d) * scale_d;
-        if (j == y) gt = gy_d;
-        ((float*)gbase)[j] = (float)gt;
+        grow[j] = (float)(exp_f64((double)((const float*)rbase)[j] - lse_d) * scale_d);
       }
     }
+    // the label's gradient overwrites the value this lane just stored for it
+    // (same lane, same address: program order)
+    const Owner own = owner<NT, EPV>(g, y, tid);
+    const float gy = (float)gy_d;
+    if (own.k >= v0 / NT && own.k < v0 / NT + VPL) ((float*)gbody)[(int64_t)(own.k * NT + tid) * EPV + own.e] = gy;
+    if (slab == 0 && own.head > 0) grow[tid] = gy;
+    if (slab == 0 && own.tail > 0) grow[g.head + (int64_t)g.nvec * EPV + tid] = gy;
   }
 }
 
@@ -1440,15 +1470,18 @@ __global__ __launch_bounds__(NT, (stats_min_waves<VPL>())) void slab_stats_kerne
     if (own.head > 0) xh = -INFINITY;
     if (own.tail > 0) xt = -INFINITY;
     const double mm = (mf == -INFINITY) ? 0.0 : (double)mf;
-    s = exp((double)xh - mm) + exp((double)xt - mm);
+    if (own.k >= 0) {  // the label is left out of the sum
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        if (k == own.k) F32::kill(v[k], own.e);
+    }
+    double s4[4] = {exp_f64((double)xh - mm), exp_f64((double)xt - mm), 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
       if (k * NT + tid < g.nvec)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const double e = exp((double)as<float>(v[k][d]) - mm);
-          s += (k == own.k && d == own.e) ? 0.0 : e;  // the label is left out
-        }
+        for (int d = 0; d < 4; ++d) s4[d] += exp_f64((double)as<float>(v[k][d]) - mm);
+    s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     m = mf;
   }
   wave_ms(m, s);
