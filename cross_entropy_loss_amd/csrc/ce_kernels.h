@@ -200,13 +200,6 @@ __device__ __forceinline__ float wave_min(float v) {
 }
 
 // Merge of two (max, sum-relative-to-max) pairs; a pair with m = -inf is empty.
-__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
-  const float M = fmaxf(m, m2);
-  const float a = (m == -INFINITY) ? 0.0f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
-  const float b = (m2 == -INFINITY) ? 0.0f : s2 * __builtin_amdgcn_exp2f((m2 - M) * kLog2e);
-  m = M;
-  s = a + b;
-}
 __device__ __forceinline__ void ms_merge(double& m, double& s, double m2, double s2) {
   const double M = fmax(m, m2);
   const double a = (m == -INFINITY) ? 0.0 : s * exp(m - M);
@@ -246,14 +239,6 @@ __device__ __forceinline__ double exp_f64(double d) {
   return (t < -1100.0) ? 0.0 : r;
 }
 
-template <typename F>
-__device__ __forceinline__ void wave_ms(F& m, F& s) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const F m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-    ms_merge(m, s, m2, s2);
-  }
-}
 __device__ __forceinline__ float first_lane(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -331,6 +316,37 @@ __device__ __forceinline__ void row_stats(float m, float s, float mn, float* lm,
 }
 
 
+
+// (max, sum) statistics of a workgroup whose lanes hold a max m (an input
+// value) and a sum s relative to it, for the fp64 sums of fp32 rows and for
+// slab partials: the workgroup max first (DPP within each wave, the waves'
+// maxima through LDS), then one rescale per lane, then the sum (shuffles
+// within each wave, the waves' sums added in wave order).  Deterministic;
+// every thread returns the same M and S.  (Merging (max, sum) pairs at every
+// shuffle step instead costs two exponentials per step and lane.)
+__device__ __forceinline__ float rescale(float s, float m, float M) {
+  return s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+}
+__device__ __forceinline__ double rescale(double s, float m, float M) { return s * exp_f64((double)m - (double)M); }
+template <int NW, typename A>
+__device__ __forceinline__ void block_ms(float m, A s, float* lm, A* ls, float& M, A& S) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const float mw = wave_reduce(m, -INFINITY, OpMax());
+  if (lane == 0) lm[wid] = mw;
+  __syncthreads();
+  float mb = lm[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mb = fmaxf(mb, lm[w]);
+  A r = (m == -INFINITY) ? (A)0 : rescale(s, m, mb);
+  r = wave_sum(r);
+  if (lane == 0) ls[wid] = r;
+  __syncthreads();
+  A t = ls[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) t += ls[w];
+  M = mb;
+  S = t;
+}
 
 // ---------------------------------------------------------------------------
 // Per-call arguments.
@@ -1201,10 +1217,11 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
 template <int NT, int VPL, int POL, bool FUSED>
 __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
   constexpr int ESZ = 4, EPV = 4, NW = NT / 64;
-  __shared__ double lds_m[NW], lds_s[NW];
+  __shared__ float lds_m[NW];
+  __shared__ double lds_s[NW];
   __shared__ uint32_t lds_u[2 * NW + 4];
   __shared__ double lds_d[NT];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint32_t epoch = ld_agent(&a.ws->epoch);
   const uint32_t tag = epoch + 1u;
@@ -1247,24 +1264,17 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
       for (int k = 0; k < VPL; ++k)
         if (k == own.k) F32::kill(v[k], own.e);
     }
-    double m = (double)mf;
-    const double mm = (mf == -INFINITY) ? 0.0 : m;
+    const double mm = (mf == -INFINITY) ? 0.0 : (double)mf;
     double s4[4] = {exp_f64((double)xh - mm), exp_f64((double)xt - mm), 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
       if (k * NT + tid < g.nvec)
 #pragma unroll
         for (int d = 0; d < 4; ++d) s4[d] += exp_f64((double)as<float>(v[k][d]) - mm);
-    double s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    wave_ms(m, s);
-    if (lane == 0) {
-      lds_m[wid] = m;
-      lds_s[wid] = s;
-    }
-    __syncthreads();
-    double M = lds_m[0], S_ex = lds_s[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) ms_merge(M, S_ex, lds_m[w], lds_s[w]);
+    float Mf;
+    double S_ex;
+    block_ms<NW>(mf, (s4[0] + s4[1]) + (s4[2] + s4[3]), lds_m, lds_s, Mf, S_ex);
+    const double M = (double)Mf;
     if (badlab) {
       lse = loss = pcomp = __builtin_nan("");
     } else {
@@ -1418,9 +1428,10 @@ __global__ __launch_bounds__(NT, (stats_min_waves<VPL>())) void slab_stats_kerne
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
   typedef typename T::acc_t A;
   typedef typename T::bits_t B;
-  __shared__ A lds_m[NW], lds_s[NW];
+  __shared__ float lds_m[NW];
+  __shared__ A lds_s[NW];
   __shared__ uint32_t lds_u[2 * NW + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t bid = blockIdx.x;
   const int64_t row = bid / a.C;
   const int c = (int)(bid % a.C);
@@ -1451,7 +1462,8 @@ __global__ __launch_bounds__(NT, (stats_min_waves<VPL>())) void slab_stats_kerne
   if (has_t) xt = T::load1(((const B*)sbase)[g.head + (int64_t)g.nvec * EPV + tid]);
   if (mine && tid == 0) a.slab_xy[row] = T::load1(((const B*)sbase)[y - j0]);
   const Owner own = owner<NT, EPV>(g, mine ? y - j0 : -1, tid);
-  A m, s;
+  float m;
+  A s;
   if constexpr (ESZ == 2) {
     float mf = fmaxf(xh, xt), mn = INFINITY;
     pass0_16<T, NT, VPL>(v, g.nvec, tid, mf, mn);
@@ -1484,17 +1496,10 @@ __global__ __launch_bounds__(NT, (stats_min_waves<VPL>())) void slab_stats_kerne
     s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     m = mf;
   }
-  wave_ms(m, s);
-  if (lane == 0) {
-    lds_m[wid] = m;
-    lds_s[wid] = s;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    A M = lds_m[0], S = lds_s[0];
-    for (int w = 1; w < NW; ++w) ms_merge(M, S, lds_m[w], lds_s[w]);
-    a.slab_ms[bid] = make_double2((double)M, (double)S);
-  }
+  float M;
+  A S;
+  block_ms<NW>(m, s, lds_m, lds_s, M, S);
+  if (tid == 0) a.slab_ms[bid] = make_double2((double)M, (double)S);
 }
 
 // Merge of the C slab partials of a row (fp64): lse, loss, pcomp.
