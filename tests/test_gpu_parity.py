@@ -84,7 +84,7 @@ def test_config1_tiny():
 
 
 RAGGED = [(d, V) for d in ("bf16", "f16") for V in (1, 2, 3, 7, 8, 9, 17, 1000, 1023, 2049, 4097, 32001)] + \
-         [("f32", V) for V in (1, 3, 4, 5, 999, 4097, 16385)]
+         [("f32", V) for V in (1, 3, 4, 5, 999, 4097, 16385, 24001, 32000, 49999, 65536)]
 
 
 @pytest.mark.parametrize("dtype,V", RAGGED, ids=[f"{d}-V{v}" for d, v in RAGGED])
