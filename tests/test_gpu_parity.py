@@ -288,6 +288,33 @@ def test_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
+NEG_INF_BITS = {"bf16": 0xFF80, "f16": 0xFC00, "f32": 0xFF800000}
+MASKED = [("bf16", 1000, 0), ("bf16", 32000, 0), ("f16", 49152, 0), ("f32", 1000, 0), ("f32", 32000, 0),
+          ("bf16", 128256, 0), ("bf16", 150001, 65536), ("f32", 70001, 0)]
+
+
+@pytest.mark.parametrize("dtype,V,chunk", MASKED, ids=[f"{d}-V{v}-c{c}" for d, v, c in MASKED])
+def test_masked_vocabulary(dtype, V, chunk):
+    # -inf logits (a masked vocabulary, and whole masked ranges of a row):
+    # they take no probability and get a +0 gradient; labels stay unmasked
+    N = 24 if V <= 32000 else 8
+    w = wl.custom(f"masked-{dtype}-{V}", 71, N, V, dtype, 2.0, 0.1)
+    bits, p = wl.make(w)
+    rng = np.random.default_rng(72)
+    mask = rng.random(bits.shape) < 0.3
+    mask[1, : V // 2] = True           # the first half of a row masked
+    mask[2, V // 2:] = True            # the second half of another
+    rows = np.arange(N)
+    valid = p.labels != -100
+    mask[rows[valid], p.labels[valid]] = False
+    bits = bits.copy()
+    bits.view(np.uint32 if dtype == "f32" else np.uint16)[mask] = NEG_INF_BITS[dtype]
+    out, g = run_fused(bits, p.labels, dtype, chunk=chunk)
+    check_against_oracle(out, g, bits, p.labels, dtype)
+    gb = to_host_bits(g, dtype)
+    assert (gb[mask & valid[:, None]] == 0).all(), "masked logits must get a +0 gradient"
+
+
 def test_concurrent_host_threads():
     # two host threads, each with its own stream and (through the binding)
     # its own workspace, call the fused entry point at the same time: one on
