@@ -648,6 +648,118 @@ def bench_rope(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+def split_bytes(w, labels) -> dict:
+    """Algorithmic bytes of the split calls: ce_forward reads each valid row
+    once (+ label, loss, lse, 1 - p_label per row); ce_backward reads each
+    valid row and writes every row (+ label, lse, 1 - p_label per row)."""
+    n_valid = int((labels != -100).sum())
+    row = w.V * w.elem_bytes
+    return {"forward": n_valid * row + 28 * w.N, "backward": (n_valid + w.N) * row + 24 * w.N}
+
+
+def profile_summary_split(d: str, workload: int) -> None:
+    """Summary of bench.py --op split runs -> profiles/ce_split_<workload>.*"""
+    import workloads as wl
+    w = wl.WORKLOADS[workload]
+    sha = kernel_sha()
+    head = _profile_header(f"split cross-entropy: ce_forward, then ce_backward in place, workload {w.name}",
+                           f"N={w.N} V={w.V} dtype={w.dtype} chunk={w.chunk}", sha, "split", workload)
+    b = split_bytes(w, wl.plan(w).labels)
+    _summarize(d, f"ce_split_{w.name}", head,
+               {"forward": (("row_kernel_16", "row_kernel_32", "slab_stats", "slab_merge"), b["forward"]),
+                "backward": (("grad_kernel",), b["backward"])},
+               w.N * w.V * w.elem_bytes, sha)
+
+
+def bench_split(args) -> None:
+    """ce_forward and ce_backward (in place, the split form of a8) timed
+    separately on one workload: logits resident in HBM, restored before and
+    L2 / MALL flushed before each call, events on the call's stream."""
+    import torch
+    import cross_entropy_loss_amd as ce
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    p = wl.plan(w)
+    bits = wl.logits(w, None, p, threads=16)
+    labels = p.labels
+    dev = torch.device("cuda:0")
+    raw = torch.from_numpy(bits.view(np.int16) if w.elem_bytes == 2 else bits.view(np.int32))
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    pristine = raw.to(dev).view(tdt)
+    work = torch.empty_like(pristine)
+    y = torch.from_numpy(labels).to(dev)
+    dloss = torch.tensor([w.dloss], dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    ws = ce.Workspace(dev, ce.ce_workspace_bytes(w.N, w.V, w.chunk, tdt))
+    out = ce._outputs(w.N, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        work.copy_(pristine)
+        flush.fill_(2 * i)
+        if ev:
+            ev[0].record(stream)
+        ce.ce_forward(work, y, -100, w.chunk, ws, out)
+        if ev:
+            ev[1].record(stream)
+        flush.fill_(2 * i + 1)
+        if ev:
+            ev[2].record(stream)
+        ce.ce_backward(work, y, out["lse_rows"], out["pcomp_rows"], out["n_valid"], dloss, -100, grad=work)
+        if ev:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = int(out["status"].item())
+    if st != 0:
+        raise SystemExit(f"kernel status {st:#x}")
+    fms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    nbytes = pristine.numel() * pristine.element_size()
+    copy_gbs = _calib_copy_gbs(pristine, work, nbytes, flush, stream, 3 if args.calibrate else 7)
+    b = split_bytes(w, labels)
+    traffic = None
+    cpath = os.path.join(ROOT, "profiles", f"ce_split_{w.name}.counters.json")
+    if os.path.exists(cpath):
+        with open(cpath) as f:
+            c = json.load(f)
+        if c.get("kernel_sha") == kernel_sha():
+            traffic = {"forward": c.get("forward_traffic_bytes"), "backward": c.get("backward_traffic_bytes")}
+
+    def roof(part, ms_mean):
+        a = b[part] / (ms_mean * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS,
+                "traffic": traffic[part] if traffic else None, "copy_ceiling": copy_gbs, "frac_of_copy": a / copy_gbs}
+
+    f_mean, b_mean = float(fms.mean()), float(bms.mean())
+    rec = {
+        "metric": f"CE split forward + backward tokens/s, N={w.N} V={w.V} {w.dtype}",
+        "value": w.N / ((f_mean + b_mean) * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": f_mean + b_mean, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.N, "vocab": w.V, "logits_dtype": w.dtype, "chunk": w.chunk,
+                   "n_valid": int((labels != -100).sum()), "calls": "ce_forward, then ce_backward in place"},
+        "roofline": roof("backward", b_mean),
+        "roofline_forward": roof("forward", f_mean),
+        "timing": {"forward_ms_mean": f_mean, "forward_ms_median": float(np.median(fms)),
+                   "backward_ms_mean": b_mean, "backward_ms_median": float(np.median(bms)),
+                   "algorithmic_bytes": b, "wall_ms_per_step_incl_restore_and_flush": wall / args.steps * 1e3,
+                   "kernel_sha": kernel_sha()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, bits, labels)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -657,9 +769,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR")
-    ap.add_argument("--op", choices=["ce", "linear", "rmsnorm", "rope"], default="ce",
-                    help="ce: the cross-entropy call (default); linear: LM-head projection + cross-entropy; "
-                         "rmsnorm: RMS layer normalisation forward + backward; rope: rotary embedding of q and k")
+    ap.add_argument("--op", choices=["ce", "split", "linear", "rmsnorm", "rope"], default="ce",
+                    help="ce: the fused cross-entropy call (default); split: ce_forward and ce_backward timed "
+                         "separately; linear: LM-head projection + cross-entropy; rmsnorm: RMS layer "
+                         "normalisation forward + backward; rope: rotary embedding of q and k")
     ap.add_argument("--chunk-rows", type=int, default=None, help="--op linear: rows per chunk")
     args = ap.parse_args()
     if args.profile_summary:
@@ -669,6 +782,8 @@ def main():
             profile_summary_norm(args.profile_summary, args.workload)
         elif args.op == "rope":
             profile_summary_rope(args.profile_summary, args.workload)
+        elif args.op == "split":
+            profile_summary_split(args.profile_summary, args.workload)
         else:
             profile_summary(args.profile_summary, args.workload)
         return
@@ -684,6 +799,9 @@ def main():
         return
     if args.op == "rope":
         bench_rope(args)
+        return
+    if args.op == "split":
+        bench_split(args)
         return
 
     import torch
