@@ -31,12 +31,15 @@ int64_t max_slab(int dtype) { return (int64_t)1024 * 16 * epv(dtype); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Vocabulary split: C slabs of width `width` (C == 1: whole rows on chip).
-// A row that fits on chip is reduced whole in one pass whatever `chunk` is:
-// its workgroup already merges (max, sum) partials of many lanes and waves,
-// a finer partition of the same log-sum-exp merge, and the result differs
-// from a per-slab merge only by rounding.  Wider rows are cut into slabs of
-// width `chunk` (default 65536 16-bit / 32768 fp32 elements) whose partials
-// are merged per row.
+// A row that fits on chip is read once whatever `chunk` is: its workgroup
+// already merges (max, sum) partials of many lanes and waves, a finer
+// partition of the same log-sum-exp merge, and the result differs from a
+// per-chunk merge only by rounding.  The fused 16-bit rows wider than 64K
+// elements reduce two chunks separately and merge them when `chunk` is half
+// the workgroup's capacity (65536); other on-chip widths reduce the row
+// whole.  Rows wider than on-chip capacity are cut into slabs of width
+// `chunk` (default 65536 16-bit / 32768 fp32 elements) whose partials are
+// merged per row.
 struct Split {
   int64_t width;
   int C;
@@ -180,6 +183,13 @@ KernelFn aligned_fn(Cfg c) {
 #undef MAKE
   return nullptr;
 }
+// Two vocabulary chunks of half the vector slots each (1024 lanes x 8 slots
+// x 8 elements = 65536 16-bit elements per chunk).
+template <typename T>
+KernelFn aligned2_fn(Cfg c) {
+  if (c.nt == 1024 && c.vpl == 16) return cek::row_fused_aligned<T, 1024, 16, kPol, 8>;
+  return nullptr;
+}
 template <bool FUSED>
 KernelFn row32_fn(Cfg c) {
 #define MAKE(NT, VPL) \
@@ -289,7 +299,12 @@ int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int
     // buffer-addressed kernel (one 1024-lane workgroup per CU sweeps rows)
     const bool aligned = ((uintptr_t)logits % 16 == 0) && ((ld * esize(dtype)) % 16 == 0) && (V % e == 0);
     if (fused && aligned && dtype != CE_DTYPE_F32 && c.nt == 1024) {
-      fn = (dtype == CE_DTYPE_BF16) ? aligned_fn<cek::BF16>(c) : aligned_fn<cek::F16>(c);
+      // a chunk of exactly half the workgroup's vector slots: the two chunks'
+      // (max, sum) are reduced separately and merged on chip
+      const bool two = chunk > 0 && chunk < V && chunk == (int64_t)c.nt * (c.vpl / 2) * e;
+      KernelFn f2 = nullptr;
+      if (two) f2 = (dtype == CE_DTYPE_BF16) ? aligned2_fn<cek::BF16>(c) : aligned2_fn<cek::F16>(c);
+      fn = f2 ? f2 : ((dtype == CE_DTYPE_BF16) ? aligned_fn<cek::BF16>(c) : aligned_fn<cek::F16>(c));
       G = persistent_grid(fn, c.nt, N);
     }
     a.K = counters_for(N, G);

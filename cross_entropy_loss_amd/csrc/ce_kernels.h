@@ -575,10 +575,12 @@ __device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t 
 // high element is read as the whole dword (its low half becomes extra
 // mantissa bits), which moves it by less than one bf16 ulp -- harmless for a
 // max used only as the stabilising shift.
-template <typename T, int NT, int VPL>
+// K0..K1: the vector slots taken (all by default; a vocabulary chunk of the
+// row otherwise).
+template <typename T, int NT, int VPL, int K0 = 0, int K1 = VPL>
 __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int tid, float& m, float& mn) {
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
+  for (int k = K0; k < K1; ++k) {
     if (k * NT + tid < nvec) {
       if constexpr (T::kBF) {
 #pragma unroll
@@ -601,13 +603,13 @@ __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int ti
 // pass 1: sum of 2^{x log2 e - mc} over the lane's elements, leaving out
 // element ex of vector kx (the label, in the lane that holds it; kx = -1
 // elsewhere).  The exclusion zeroes that term; the staged data is untouched.
-template <typename T, int NT, int VPL>
+template <typename T, int NT, int VPL, int K0 = 0, int K1 = VPL>
 __device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int tid, float mc, float xh, float xt,
                                          int kx = -1, int ex = 0) {
   float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xh, kLog2e, -mc));
   float s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -mc));
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
+  for (int k = K0; k < K1; ++k) {
     if (k * NT + tid < nvec) {
       float t[8];
 #pragma unroll
@@ -1132,7 +1134,13 @@ __device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_
   }
 }
 
-template <typename T, int NT, int VPL, int POL>
+//
+// KB > 0: the vocabulary is taken as two chunks, vector slots [0, KB) and
+// [KB, VPL) of every lane (chunk width KB * NT * 8 elements): each chunk's
+// (max, label-excluded sum) is reduced over the workgroup on its own and the
+// two are merged, the per-chunk log-sum-exp merge of a chunked loss done
+// on chip with no second read of the row.
+template <typename T, int NT, int VPL, int POL, int KB = 0>
 __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV, NW = NT / 64;
   __shared__ float lds_m[2][NW], lds_s[2][NW], lds_mn[2][NW];
@@ -1162,8 +1170,6 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
     float lse = 0.0f, loss = 0.0f, pcomp = 0.0f;
     if (!ignored) {
       const float xy = bad ? 0.0f : T::load1(((const typename T::bits_t*)base)[y]);
-      float m = -INFINITY, mn = INFINITY;
-      pass0_16<T, NT, VPL>(v, nvec, tid, m, mn);
       int kx = -1, ex = 0;
       if (!bad) {
         const int vy = (int)(y / EPV);
@@ -1172,11 +1178,31 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
           ex = (int)(y % EPV);
         }
       }
-      const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-      const float s = pass1_16<T, NT, VPL>(v, nvec, tid, mc, -INFINITY, -INFINITY, kx, ex);
       float M, S_ex, MN;
-      row_stats<NW>(m, s, mn, lds_m[par], lds_s[par], lds_mn[par], M, S_ex, MN);
-      par ^= 1;
+      float m = -INFINITY, mn = INFINITY;
+      if constexpr (KB == 0) {
+        pass0_16<T, NT, VPL>(v, nvec, tid, m, mn);
+        const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
+        const float s = pass1_16<T, NT, VPL>(v, nvec, tid, mc, -INFINITY, -INFINITY, kx, ex);
+        row_stats<NW>(m, s, mn, lds_m[par], lds_s[par], lds_mn[par], M, S_ex, MN);
+        par ^= 1;
+      } else {
+        // chunk by chunk (each its own max), then the two (max, sum) merged;
+        // the two reductions take both LDS slots, so par is left as it is
+        float m1 = -INFINITY, mn1 = INFINITY;
+        pass0_16<T, NT, VPL, 0, KB>(v, nvec, tid, m, mn);
+        pass0_16<T, NT, VPL, KB, VPL>(v, nvec, tid, m1, mn1);
+        const float mc0 = (m == -INFINITY) ? 0.0f : m * kLog2e, mc1 = (m1 == -INFINITY) ? 0.0f : m1 * kLog2e;
+        const float s0 = pass1_16<T, NT, VPL, 0, KB>(v, nvec, tid, mc0, -INFINITY, -INFINITY, kx, ex);
+        const float s1 = pass1_16<T, NT, VPL, KB, VPL>(v, nvec, tid, mc1, -INFINITY, -INFINITY, kx, ex);
+        float M0, S0, MN0, M1, S1, MN1;
+        row_stats<NW>(m, s0, mn, lds_m[par], lds_s[par], lds_mn[par], M0, S0, MN0);
+        row_stats<NW>(m1, s1, mn1, lds_m[par ^ 1], lds_s[par ^ 1], lds_mn[par ^ 1], M1, S1, MN1);
+        M = fmaxf(M0, M1);
+        S_ex = ((M0 == -INFINITY) ? 0.0f : S0 * __builtin_amdgcn_exp2f((M0 - M) * kLog2e)) +
+               ((M1 == -INFINITY) ? 0.0f : S1 * __builtin_amdgcn_exp2f((M1 - M) * kLog2e));
+        MN = fminf(MN0, MN1);
+      }
       if (bad) {
         lse = loss = pcomp = __builtin_nanf("");
         buf_fill_row<NT, VPL, POL>(rs, voff, (T::ESZ == 2) ? 0x7fc07fc0u : 0x7fc00000u);

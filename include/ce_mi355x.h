@@ -107,9 +107,12 @@ int ce_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *                 (lse = M + log sum_c exp(lse_c - M), M = max_c lse_c; PR #79
  *                 "TODO": chunked loss) of rows too wide to be held on chip
  *                 (> 131072 bf16/fp16 or > 65536 fp32 elements); 0 = 65536
- *                 (fp32: 32768).  A row that fits on chip is reduced whole in
- *                 one pass whatever chunk is: its workgroup merges (max, sum)
- *                 partials of many lanes, a finer partition of the same merge.
+ *                 (fp32: 32768).  A row that fits on chip is read once
+ *                 whatever chunk is: its workgroup merges (max, sum) partials
+ *                 of many lanes, a finer partition of the same merge.  In
+ *                 ce_fwd_bwd_inplace, 16-byte-aligned bf16/fp16 rows of
+ *                 65537..131072 elements with chunk = 65536 reduce the two
+ *                 chunks separately and merge their (max, sum) on chip.
  *                 The result does not depend on chunk beyond rounding.
  *   loss_mean     out, 1 float: L (NaN when n_valid == 0).
  *   loss_rows     out, n_rows floats: per-row loss (0 for ignored rows).

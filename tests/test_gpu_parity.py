@@ -258,10 +258,12 @@ def test_gradient_modes(dtype, V, sigma, n, dloss):
     check_against_oracle(f, grad, bits, p.labels, dtype, dloss=dloss)
 
 
-def test_wide_rows_repeated_calls():
-    # the persistent buffer-store kernel (rows of 128256 bf16 elements): every
-    # call must reproduce the oracle and the first call bit for bit (its store
-    # data registers are rewritten right after each store)
+@pytest.mark.parametrize("chunk", [0, 65536])
+def test_wide_rows_repeated_calls(chunk):
+    # the persistent buffer-store kernel (rows of 128256 bf16 elements, whole
+    # or as two 65536-wide chunks): every call must reproduce the oracle and
+    # the first call bit for bit (its store data registers are rewritten
+    # right after each store)
     w = wl.WORKLOADS[4]
     p = wl.plan(w)
     rows = np.arange(96)
@@ -269,7 +271,7 @@ def test_wide_rows_repeated_calls():
     labels = p.labels[rows]
     first = None
     for i in range(6):
-        out, g = run_fused(bits, labels, w.dtype, dloss=w.dloss)
+        out, g = run_fused(bits, labels, w.dtype, dloss=w.dloss, chunk=chunk)
         gb = to_host_bits(g, w.dtype)
         if first is None:
             check_against_oracle(out, g, bits, labels, w.dtype, dloss=w.dloss)
@@ -290,7 +292,8 @@ def test_deterministic():
 
 NEG_INF_BITS = {"bf16": 0xFF80, "f16": 0xFC00, "f32": 0xFF800000}
 MASKED = [("bf16", 1000, 0), ("bf16", 32000, 0), ("f16", 49152, 0), ("f32", 1000, 0), ("f32", 32000, 0),
-          ("bf16", 128256, 0), ("bf16", 150001, 65536), ("f32", 70001, 0)]
+          ("bf16", 128256, 0), ("bf16", 128256, 65536), ("f16", 128256, 65536), ("bf16", 150001, 65536),
+          ("f32", 70001, 0)]
 
 
 @pytest.mark.parametrize("dtype,V,chunk", MASKED, ids=[f"{d}-V{v}-c{c}" for d, v, c in MASKED])
@@ -304,6 +307,7 @@ def test_masked_vocabulary(dtype, V, chunk):
     mask = rng.random(bits.shape) < 0.3
     mask[1, : V // 2] = True           # the first half of a row masked
     mask[2, V // 2:] = True            # the second half of another
+    mask[3, : min(V, 65536)] = True    # a whole first vocabulary chunk
     rows = np.arange(N)
     valid = p.labels != -100
     mask[rows[valid], p.labels[valid]] = False
