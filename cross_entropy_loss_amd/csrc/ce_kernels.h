@@ -193,11 +193,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
   return v;
 }
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 
 // Merge of two (max, sum-relative-to-max) pairs; a pair with m = -inf is empty.
 __device__ __forceinline__ void ms_merge(double& m, double& s, double m2, double s2) {
@@ -661,18 +656,17 @@ __device__ __forceinline__ float gelem(float x, const GradConsts& k) {
   else return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -k.lcs)) * k.ss;
 }
 
-// Next-row prefetch issued from pass 2: once vector k of the current row has
-// been consumed, the same registers receive vector k of the next row.
+// A row's 16-byte-aligned body to load: its first vector and vector count.
 struct Prefetch {
-  const u32x4* body;  // next row's aligned body (NULL: nothing to fetch)
+  const u32x4* body;  // NULL: nothing to load
   int nvec;
 };
 
 // pass 2: gradient of the staged vectors, stored to gbody.  The label element
 // (held by lane/vector `own`) gets k.gy.
 template <typename T, int NT, int VPL, int POL, int MODE>
-__device__ __forceinline__ void pass2_16(u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
-                                         const Owner& own, const Prefetch& pf) {
+__device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
+                                         const Owner& own) {
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     const int idx = k * NT + tid;
@@ -692,10 +686,10 @@ __device__ __forceinline__ void pass2_16(u32x4 (&v)[VPL], int nvec, int tid, u32
       for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
       stv<POL>(gbody + idx, o);
     }
-    // keep the prefetch after this vector's arithmetic: hoisting it would
-    // hold the old and the new row in registers at once
+    // one vector's arithmetic and store at a time: left to itself the
+    // scheduler interleaves vectors and holds more values live (this shape
+    // is tuned with the barrier in place)
     __builtin_amdgcn_sched_barrier(0);
-    if (pf.body && idx < pf.nvec) v[k] = ldv<POL>(pf.body + idx);
   }
 }
 
@@ -771,19 +765,18 @@ __device__ __forceinline__ void nan_row(char* gbase, const Geom& g, int tid, int
 template <typename T, int NT, int VPL, int POL>
 __device__ __forceinline__ void grad_row_16(u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, int mode,
                                             const GradConsts& kc, const Owner& own, float xh, float xt,
-                                            typename T::bits_t* ph, typename T::bits_t* pt,
-                                            const Prefetch& pf = Prefetch{nullptr, 0}) {
+                                            typename T::bits_t* ph, typename T::bits_t* pt) {
   float gh = 0.0f, gt = 0.0f;
   if (mode == kFold) {
-    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own, pf);
+    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own);
     gh = gscalar<T, kFold>(xh, own.head > 0, kc);
     gt = gscalar<T, kFold>(xt, own.tail > 0, kc);
   } else if (mode == kMul) {
-    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own, pf);
+    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own);
     gh = gscalar<T, kMul>(xh, own.head > 0, kc);
     gt = gscalar<T, kMul>(xt, own.tail > 0, kc);
   } else {
-    pass2_16<T, NT, VPL, POL, kScaled>(v, nvec, tid, gbody, kc, own, pf);
+    pass2_16<T, NT, VPL, POL, kScaled>(v, nvec, tid, gbody, kc, own);
     gh = gscalar<T, kScaled>(xh, own.head > 0, kc);
     gt = gscalar<T, kScaled>(xt, own.tail > 0, kc);
   }
@@ -1088,7 +1081,6 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_f32_to16_k
 // per-vector 64-bit addresses are held in VGPRs.  The descriptor's size also
 // bounds every access: loads past the row return 0 and stores past it are
 // dropped, so only the reductions of pass 0 / pass 1 need lane predicates.
-// The next row's loads are issued from pass 2 (see Prefetch above).
 // ---------------------------------------------------------------------------
 // row_rsrc, aux_load / aux_store and buf_store: ce_buffer.h
 
@@ -1105,12 +1097,11 @@ __device__ __forceinline__ void buf_fill_row(__amdgpu_buffer_rsrc_t rs, uint32_t
   for (int k = 0; k < VPL; ++k) buf_store<aux_store<POL>()>(z, rs, voff, k * NT * 16);
 }
 
-// pass 2 on buffer stores, optionally with the next row's loads issued into
-// the registers each vector frees.  Lanes past the row compute garbage that
-// their dropped stores discard.
-template <typename T, int NT, int VPL, int POL, bool PF, int MODE>
-__device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t out, __amdgpu_buffer_rsrc_t nxt,
-                                          uint32_t voff, const GradConsts& kc, int kx, int ex) {
+// pass 2 on buffer stores.  Lanes past the row compute garbage that their
+// dropped stores discard.
+template <typename T, int NT, int VPL, int POL, int MODE>
+__device__ __forceinline__ void pass2_buf(const u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_t out, uint32_t voff,
+                                          const GradConsts& kc, int kx, int ex) {
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     float gv[8];
@@ -1127,10 +1118,6 @@ __device__ __forceinline__ void pass2_buf(u32x4 (&v)[VPL], __amdgpu_buffer_rsrc_
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[d] = T::pack(gv[2 * d], gv[2 * d + 1]);
     buf_store<aux_store<POL>()>(o, out, voff, k * NT * 16);
-    if constexpr (PF) {
-      __builtin_amdgcn_sched_barrier(0);
-      v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nxt, voff, k * NT * 16, aux_load<POL>()));
-    }
   }
 }
 
@@ -1217,9 +1204,9 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
         const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
         const int mode = grad_mode<T>(scale, tmin);
-        if (mode == kFold) pass2_buf<T, NT, VPL, POL, false, kFold>(v, rs, rs, voff, kc, kx, ex);
-        else if (mode == kScaled) pass2_buf<T, NT, VPL, POL, false, kScaled>(v, rs, rs, voff, kc, kx, ex);
-        else pass2_buf<T, NT, VPL, POL, false, kMul>(v, rs, rs, voff, kc, kx, ex);
+        if (mode == kFold) pass2_buf<T, NT, VPL, POL, kFold>(v, rs, voff, kc, kx, ex);
+        else if (mode == kScaled) pass2_buf<T, NT, VPL, POL, kScaled>(v, rs, voff, kc, kx, ex);
+        else pass2_buf<T, NT, VPL, POL, kMul>(v, rs, voff, kc, kx, ex);
       }
     } else {
       buf_fill_row<NT, VPL, POL>(rs, voff, 0u);
