@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
-BASELINE_METRIC = "CE fwd+bwd tokens/s and HBM GB/s (% of peak), N=4096 V=32000 bf16"
+HEADLINE_METRIC = "CE fwd+bwd tokens/s and HBM GB/s (% of peak), N=4096 V=32000 bf16"
 KERNEL_SOURCES = ["cross_entropy_loss_amd/csrc/ce_kernels.h", "cross_entropy_loss_amd/csrc/ce_buffer.h",
                   "cross_entropy_loss_amd/csrc/ce_api.hip"]
 
@@ -788,7 +788,7 @@ def main():
             profile_summary(args.profile_summary, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     if args.op == "linear":
@@ -871,7 +871,7 @@ def main():
     abytes = algorithmic_bytes(w, labels)
     achieved = abytes / (ms_mean * 1e-3) / 1e9
     rec = {
-        "metric": BASELINE_METRIC,
+        "metric": HEADLINE_METRIC,
         "value": w.N / (ms_mean * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,

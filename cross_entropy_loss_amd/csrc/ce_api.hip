@@ -377,7 +377,7 @@ const char* ce_error_string(int code) {
     case CE_ERR_INVALID_ARG: return "invalid argument (size, stride, pointer or alignment)";
     case CE_ERR_DTYPE: return "unknown dtype";
     case CE_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than ce_workspace_bytes()";
-    case CE_ERR_UNSUPPORTED: return "request not served by this build";
+    case CE_ERR_UNSUPPORTED: return "request not served by this library";
     case CE_ERR_HIP: return "HIP runtime error";
     default: return "unknown error code";
   }

@@ -72,7 +72,7 @@ enum ce_error {
   CE_ERR_INVALID_ARG = 1, /* bad size, stride, pointer or alignment */
   CE_ERR_DTYPE = 2,       /* unknown dtype */
   CE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than ce_workspace_bytes() */
-  CE_ERR_UNSUPPORTED = 4, /* a valid request this build does not serve */
+  CE_ERR_UNSUPPORTED = 4, /* a valid request this library does not serve */
   CE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 };
 
