@@ -41,6 +41,20 @@ def test_norm_and_rope_bytes():
     assert bench.rope_bytes(rw) == 2 * 4096 * (32 + 8) * 128 * 2 + 8 * 4096
 
 
+def test_split_call_bytes():
+    # ce_forward reads each valid row once; ce_backward reads each valid row
+    # and writes every row (ignored rows get zeros); per-row labels and
+    # statistics on top
+    w = wl.WORKLOADS[2]
+    labels = wl.plan(w).labels
+    n_valid = int((labels != -100).sum())
+    b = bench.split_bytes(w, labels)
+    assert b["forward"] == n_valid * w.V * 2 + 28 * w.N
+    assert b["backward"] == (n_valid + w.N) * w.V * 2 + 24 * w.N
+    # the pair moves one row read more than the fused call
+    assert b["forward"] + b["backward"] - bench.algorithmic_bytes(w, labels) == n_valid * w.V * 2 + 24 * w.N
+
+
 def _fake_profile(d, kernel, calib_kib_read, calib_kib_write, k_read, k_write, durations_ns):
     os.makedirs(d, exist_ok=True)
     con = sqlite3.connect(os.path.join(d, "trace_results.db"))
