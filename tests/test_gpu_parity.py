@@ -181,6 +181,28 @@ def test_no_valid_rows():
     assert (to_host_bits(g, "bf16") == 0).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_zero_and_one_rows(dtype):
+    # an empty batch: L = NaN (0/0), n_valid 0, status 0, through all three
+    # entry points; then a batch of one row against the oracle
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    _say(f"[zero rows] {dtype}")
+    x = torch.empty((0, 1000), dtype=tdt, device="cuda")
+    y = torch.empty(0, dtype=torch.int64, device="cuda")
+    fused = ce.ce_fwd_bwd_inplace(x, y)
+    f = ce.ce_forward(x, y)
+    g = ce.ce_backward(x, y, f["lse_rows"], f["pcomp_rows"], f["n_valid"])
+    torch.cuda.synchronize()
+    for o in (fused, f):
+        assert int(o["n_valid"].item()) == 0 and int(o["status"].item()) == 0
+        assert math.isnan(float(o["loss_mean"].item()))
+    assert g.shape == (0, 1000)
+    w = wl.custom(f"one-{dtype}", 81, 1, 1000, dtype, 2.0, 0.0)
+    bits, p = wl.make(w)
+    out, gg = run_fused(bits, p.labels, dtype)
+    check_against_oracle(out, gg, bits, p.labels, dtype)
+
+
 @pytest.mark.parametrize("dloss", [0.0, -1.0, 0.5, 65536.0])
 def test_dloss_values(dloss):
     w = wl.custom("dloss", 23, 40, 1000, "bf16", 2.0, 0.1)
