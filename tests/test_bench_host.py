@@ -103,3 +103,36 @@ def test_traffic_is_dropped_when_the_kernel_changed(tmp_path, monkeypatch):
     src.write_text("kernel v2")
     assert bench.measured_traffic("x", [str(src)]) is None
     assert np.isfinite(bench.HBM_PEAK_GBS) and bench.HBM_PEAK_GBS == 8000.0
+
+
+def test_split_summary_attributes_both_calls(tmp_path, monkeypatch):
+    # the split leg's summary: forward-pass kernels and the backward kernel
+    # are attributed to their own call, each scaled by the copy's counters
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_sha", lambda sources=None: "abc")
+    d = tmp_path / "db"
+    os.makedirs(d)
+    fwd, bwd = "void cek::row_kernel_16<cek::BF16, 512, 8, 3, false>(cek::Args)", "void cek::grad_kernel<...>(cek::Args)"
+    con = sqlite3.connect(str(d / "trace_results.db"))
+    con.execute("create table kernels (name text, start integer, end integer, duration integer)")
+    for name, dur in ((fwd, 50_000), (bwd, 90_000), (fwd, 52_000), (bwd, 91_000), (fwd, 51_000), (bwd, 89_000)):
+        con.execute("insert into kernels values (?, 0, ?, ?)", (name, dur, dur))
+    con.commit()
+    con.close()
+    for tag, counter, calib, kf, kb in (("fetch", "FETCH_SIZE", 128000.0, 120000.0, 121000.0),
+                                        ("write", "WRITE_SIZE", 256000.0, 0.0, 256000.0)):
+        con = sqlite3.connect(str(d / f"{tag}_results.db"))
+        con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+        for name, v in (("calib_copy_kernel(...)", calib), (fwd, kf), (bwd, kb)):
+            con.execute("insert into counters_collection values (?, ?, ?)", (name, counter, v))
+        con.commit()
+        con.close()
+    bench.profile_summary_split(str(d), 2)
+    with open(tmp_path / "profiles" / "ce_split_mistral7b-b4s1024-bf16.counters.json") as f:
+        rec = json.load(f)
+    nbytes = 4096 * 32000 * 2
+    assert rec["read_factor"] == pytest.approx(nbytes / 1024 / 128000.0)
+    assert rec["forward_traffic_bytes"] == pytest.approx(120000.0 * 1024 * rec["read_factor"])
+    assert rec["backward_traffic_bytes"] == pytest.approx(121000.0 * 1024 * rec["read_factor"] +
+                                                          256000.0 * 1024 * rec["write_factor"])
+    assert rec["forward_us"] == pytest.approx(51.0) and rec["backward_us"] == pytest.approx(90.0)
