@@ -161,7 +161,7 @@ def profile_summary_linear(d: str, workload: int) -> None:
         per_call = s / calls / 1e6
         total += per_call
         rate = ""
-        if name.startswith("Cijk_"):
+        if name.startswith(("Cijk_", "Custom_Cijk_")):  # the library GEMMs (Tensile kernel names)
             rate = f"{flops_per_gemm / (per_call * 1e-3) / 1e12:8.0f}"
         lines.append(f"  {name[:72]:72s} {n // calls:8d} {per_call:9.3f} {rate:>8s}")
     lines.append(f"  {'total':72s} {'':8s} {total:9.3f} {3 * flops_per_gemm / (total * 1e-3) / 1e12:8.0f}")

@@ -197,8 +197,11 @@ int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t 
  *   workspace     ce_linear_workspace_bytes(...) bytes, 256-byte aligned,
  *                 prepared once with ce_workspace_init: the cross-entropy
  *                 workspace of a chunk, a chunk of fp32 logits and, for
- *                 bf16/fp16, the chunk's rounded gradient and the fp32
- *                 grad_weight accumulator (vocab x hidden_size x 4 bytes).
+ *                 bf16/fp16, the chunk's rounded gradient, the fp32
+ *                 grad_weight accumulator (vocab x hidden_size x 4 bytes,
+ *                 several chunks only) and, when n_rows, hidden_size and vocab
+ *                 are multiples of 64, transposed copies of the chunk's
+ *                 gradient and hidden rows for the weight-gradient GEMM.
  * GEMMs: hipBLASLt for bf16 / fp16 (its first heuristic algorithm among those
  * needing no workspace), rocBLAS for fp32 and for shapes hipBLASLt has no
  * algorithm for; both accumulate in fp32 without atomics (repeated calls give

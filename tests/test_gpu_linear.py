@@ -145,7 +145,10 @@ def check(out, h, w, y, dtype, dloss=1.0, expect_status=0):
 # fp32 step followed by a cast
 CASES = [("bf16", 256, 384, 3000, 0), ("bf16", 300, 256, 5000, 128), ("f16", 200, 320, 4000, 64),
          ("f32", 130, 192, 2500, 64), ("bf16", 64, 128, 32000, 0), ("bf16", 513, 512, 1000, 256),
-         ("bf16", 150, 192, 3001, 64), ("f16", 140, 160, 2999, 64)]
+         ("bf16", 150, 192, 3001, 64), ("f16", 140, 160, 2999, 64),
+         # rows, hidden and vocab multiples of 64: the weight gradient from transposed operands (TN GEMM),
+         # one chunk and several
+         ("bf16", 256, 256, 4096, 0), ("bf16", 320, 192, 2048, 128), ("f16", 192, 256, 3072, 64)]
 
 
 @pytest.mark.parametrize("dtype,N,H,V,chunk", CASES, ids=[f"{d}-N{n}-H{h}-V{v}-c{c}" for d, n, h, v, c in CASES])
