@@ -164,6 +164,14 @@ def test_linear_strided_and_dloss():
     check(out, h, w, y, "bf16", dloss=0.37)
 
 
+@pytest.mark.parametrize("ldh", [136, 131])
+def test_linear_tn_strided_hidden(ldh):
+    # shapes that tile by 64: a hidden row stride that keeps 16-byte rows takes the weight gradient from
+    # transposed operands (TN GEMM), one that does not takes the NT form on the stored operands
+    h, w, y = make(26, 128, 128, 2048, "bf16")
+    check(run(h, w, y, "bf16", chunk_rows=64, ldh=ldh), h, w, y, "bf16")
+
+
 def test_linear_one_gradient_only():
     h, w, y = make(22, 100, 128, 1500, "bf16")
     a = run(h, w, y, "bf16", chunk_rows=64, want_grad_weight=False)
