@@ -415,24 +415,30 @@ class FastRoPE(torch.nn.Module):
 
 class _CrossEntropy(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, logits, labels, ignore_index, chunk):
+    def forward(ctx, logits, labels, ignore_index, chunk, inplace_backward):
         out = ce_forward(logits, labels, ignore_index, chunk)
         ctx.save_for_backward(logits, labels, out["lse_rows"], out["pcomp_rows"], out["n_valid"])
         ctx.ignore_index = ignore_index
+        ctx.inplace_backward = inplace_backward
         return out["loss_mean"][0].to(logits.dtype)
 
     @staticmethod
     def backward(ctx, g):
         logits, labels, lse, pcomp, n = ctx.saved_tensors
         dloss = g.reshape(1).to(torch.float32)
-        grad = ce_backward(logits, labels, lse, pcomp, n, dloss, ctx.ignore_index)
-        return grad, None, None, None
+        grad = ce_backward(logits, labels, lse, pcomp, n, dloss, ctx.ignore_index,
+                           grad=logits if ctx.inplace_backward else None)
+        return grad, None, None, None, None
 
 
 def cross_entropy(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
-                  chunk: int = 0) -> torch.Tensor:
-    """Token-mean softmax cross-entropy with autograd (logits [rows, vocab])."""
-    return _CrossEntropy.apply(logits, labels, ignore_index, chunk)
+                  chunk: int = 0, inplace_backward: bool = False) -> torch.Tensor:
+    """Token-mean softmax cross-entropy with autograd (logits [rows, vocab]).
+
+    inplace_backward: the backward writes the gradient over the logits'
+    storage instead of a new tensor (no second [rows, vocab] buffer; the
+    logits must not be read after the backward)."""
+    return _CrossEntropy.apply(logits, labels, ignore_index, chunk, inplace_backward)
 
 
 class FastCrossEntropyLoss(torch.nn.Module):
@@ -440,13 +446,15 @@ class FastCrossEntropyLoss(torch.nn.Module):
     over [..., vocab] logits and [...] int64 labels."""
 
     def __init__(self, ignore_index: int = -100, reduction: str = "mean", chunk: int = 0,
-                 weight=None, label_smoothing: float = 0.0):
+                 weight=None, label_smoothing: float = 0.0, inplace_backward: bool = False):
         super().__init__()
         if reduction != "mean" or weight is not None or label_smoothing != 0.0:
             raise NotImplementedError("only reduction='mean' without weights or label smoothing")
         self.ignore_index = ignore_index
         self.chunk = chunk
+        self.inplace_backward = inplace_backward
 
     def forward(self, logits: torch.Tensor, labels: torch.Tensor) -> torch.Tensor:
         V = logits.shape[-1]
-        return cross_entropy(logits.reshape(-1, V), labels.reshape(-1), self.ignore_index, self.chunk)
+        return cross_entropy(logits.reshape(-1, V), labels.reshape(-1), self.ignore_index, self.chunk,
+                             self.inplace_backward)

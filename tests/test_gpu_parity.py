@@ -418,6 +418,30 @@ def test_autograd_module():
     assert_grad_close(to_host_bits(x.grad, "bf16"), ref["grad"], "bf16", "autograd grad")
 
 
+def test_autograd_inplace_backward():
+    # the module's backward written over the logits' storage: the same
+    # gradient as the out-of-place backward, and no second buffer
+    w = wl.custom("autograd-inplace", 57, 2 * 40, 5000, "bf16", 2.0, 0.1)
+    bits, p = wl.make(w)
+    _say("[autograd in place] bf16 80x5000")
+    y = torch.from_numpy(p.labels).cuda()
+    x0 = to_device(bits, "bf16").clone().requires_grad_(True)
+    ce.FastCrossEntropyLoss()(x0.view(2, 40, 5000), y.view(2, 40)).mul(2.0).backward()
+    logits = to_device(bits, "bf16").clone()
+    h = torch.nn.Parameter(torch.zeros(1, device="cuda"))  # a non-leaf logits tensor: logits + 0 * h
+    z = logits + (h * 0).to(torch.bfloat16)
+    z.retain_grad()
+    L = ce.FastCrossEntropyLoss(inplace_backward=True)(z.view(2, 40, 5000), y.view(2, 40))
+    (L * 2.0).backward()
+    torch.cuda.synchronize()
+    # the logits' own storage now holds the gradient (z.grad itself is a copy
+    # autograd keeps for retain_grad)
+    assert torch.equal(z.detach(), x0.grad), "the gradient must be written over the logits"
+    assert torch.equal(z.grad, x0.grad)
+    ref = oracle.cross_entropy(bits, p.labels, "bf16", dloss=2.0)
+    assert_grad_close(to_host_bits(z.grad, "bf16"), ref["grad"], "bf16", "in-place autograd grad")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, in the launch configuration the benchmark times:
 # the mean and n_valid against the oracle over every row, the gradient of a
