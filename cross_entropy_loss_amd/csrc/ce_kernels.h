@@ -595,9 +595,23 @@ __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int ti
   }
 }
 
-// pass 1: sum of 2^{x log2 e - mc} over the lane's elements, leaving out
-// element ex of vector kx (the label, in the lane that holds it; kx = -1
-// elsewhere).  The exclusion zeroes that term; the staged data is untouched.
+// The label element (vector slot kx, element ex of this lane; kx = -1 in
+// the other lanes) set to -inf in the staged registers, once per row after
+// pass 0: pass 1 then sums without it (2^-inf = 0) and pass 2 writes 0 there,
+// which the owner lane overwrites with the label's gradient after the row's
+// stores.  No per-element select remains in either pass.
+template <typename T, int VPL>
+__device__ __forceinline__ void kill_label(u32x4 (&v)[VPL], int kx, int ex) {
+  if (kx < 0) return;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k)
+    if (k == kx) T::kill(v[k], ex);
+}
+
+// pass 1: sum of 2^{x log2 e - mc} over the lane's elements (the label
+// already set to -inf by kill_label; or, with kx >= 0, its term zeroed here:
+// the persistent wide-row and slab-statistics kernels keep the staged data
+// untouched, where the register kill cost them 20-30 VGPRs and spills).
 template <typename T, int NT, int VPL, int K0 = 0, int K1 = VPL>
 __device__ __forceinline__ float pass1_16(const u32x4 (&v)[VPL], int nvec, int tid, float mc, float xh, float xt,
                                          int kx = -1, int ex = 0) {
@@ -662,11 +676,10 @@ struct Prefetch {
   int nvec;
 };
 
-// pass 2: gradient of the staged vectors, stored to gbody.  The label element
-// (held by lane/vector `own`) gets k.gy.
+// pass 2: gradient of the staged vectors, stored to gbody (the label element
+// is written afterwards by grad_row_16).
 template <typename T, int NT, int VPL, int POL, int MODE>
-__device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc,
-                                         const Owner& own) {
+__device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int tid, u32x4* gbody, const GradConsts& kc) {
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     const int idx = k * NT + tid;
@@ -676,10 +689,6 @@ __device__ __forceinline__ void pass2_16(const u32x4 (&v)[VPL], int nvec, int ti
       for (int d = 0; d < 4; ++d) {
         gv[2 * d] = gelem<MODE>(T::lo(v[k][d]), kc);
         gv[2 * d + 1] = gelem<MODE>(T::hi(v[k][d]), kc);
-      }
-      if (k == own.k) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = (e == own.e) ? kc.gy : gv[e];
       }
       u32x4 o;
 #pragma unroll
@@ -768,20 +777,23 @@ __device__ __forceinline__ void grad_row_16(u32x4 (&v)[VPL], int nvec, int tid, 
                                             typename T::bits_t* ph, typename T::bits_t* pt) {
   float gh = 0.0f, gt = 0.0f;
   if (mode == kFold) {
-    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kFold>(v, nvec, tid, gbody, kc);
     gh = gscalar<T, kFold>(xh, own.head > 0, kc);
     gt = gscalar<T, kFold>(xt, own.tail > 0, kc);
   } else if (mode == kMul) {
-    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kMul>(v, nvec, tid, gbody, kc);
     gh = gscalar<T, kMul>(xh, own.head > 0, kc);
     gt = gscalar<T, kMul>(xt, own.tail > 0, kc);
   } else {
-    pass2_16<T, NT, VPL, POL, kScaled>(v, nvec, tid, gbody, kc, own);
+    pass2_16<T, NT, VPL, POL, kScaled>(v, nvec, tid, gbody, kc);
     gh = gscalar<T, kScaled>(xh, own.head > 0, kc);
     gt = gscalar<T, kScaled>(xt, own.tail > 0, kc);
   }
   if (ph) *ph = T::store1(gh);
   if (pt) *pt = T::store1(gt);
+  // the label element: after the vector store that covered it (same lane,
+  // same address, program order)
+  if (own.k >= 0) ((typename T::bits_t*)gbody)[(int64_t)(own.k * NT + tid) * T::EPV + own.e] = T::store1(kc.gy);
 }
 
 // Lane minimum of 16-bit staged vectors (bf16 only; a lower bound within one
@@ -897,7 +909,8 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
     // lane that holds it); the staged data itself is not modified
     const float xh1 = (own.head > 0) ? -INFINITY : xh, xt1 = (own.tail > 0) ? -INFINITY : xt;
     const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-    const float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh1, xt1, own.k, own.e);
+    kill_label<T, VPL>(v, own.k, own.e);
+    const float s = pass1_16<T, NT, VPL>(v, g.nvec, tid, mc, xh1, xt1);
     float M, S_ex, MN;
     row_stats<NW>(m, s, mn, lds_m, lds_s, lds_mn, M, S_ex, MN);
     if (badlab) {
