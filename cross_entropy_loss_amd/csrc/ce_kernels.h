@@ -905,8 +905,8 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
     if (has_t) mn = fminf(mn, xt);
     pass0_16<T, NT, VPL>(v, g.nvec, tid, m, mn);
     const Owner own = owner<NT, EPV>(g, badlab ? -1 : y, tid);
-    // the label element is left out of the sum (its term is zeroed in the
-    // lane that holds it); the staged data itself is not modified
+    // the label element is left out of the sum: -inf in the registers of the
+    // lane that holds it (kill_label), or in the head / tail element
     const float xh1 = (own.head > 0) ? -INFINITY : xh, xt1 = (own.tail > 0) ? -INFINITY : xt;
     const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
     kill_label<T, VPL>(v, own.k, own.e);
