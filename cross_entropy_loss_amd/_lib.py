@@ -14,12 +14,13 @@ CE_DTYPE_F32, CE_DTYPE_BF16, CE_DTYPE_F16 = 0, 1, 2
 CE_OK, CE_ERR_INVALID_ARG, CE_ERR_DTYPE, CE_ERR_WORKSPACE, CE_ERR_UNSUPPORTED, CE_ERR_HIP = range(6)
 CE_STATUS_LABEL_RANGE = 0x1
 CE_STATUS_SYNC_TIMEOUT = 0x2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # every symbol the header declares, with its C signature
 _i64, _int, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 SIGNATURES = {
     "ce_abi_version": ([], _int),
+    "ce_debug_sync_override": ([_int, _int], _int),
     "ce_error_string": ([_int], ctypes.c_char_p),
     "ce_workspace_bytes": ([_i64, _i64, _i64, _int], _sz),
     "ce_workspace_init": ([_vp, _sz, _vp], _int),

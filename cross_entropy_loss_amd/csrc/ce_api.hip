@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "ce_internal.h"
@@ -247,10 +248,26 @@ KernelFn slab_grad_fn(int dtype, Cfg c) {
   return nullptr;  // fp32 chunked rows take forward + backward
 }
 
+// Test hook state (ce_debug_sync_override): a spin limit other than the
+// default and extra partial-count words that no workgroup publishes.
+std::atomic<int> g_spin_limit{0};
+std::atomic<int> g_extra_counters{0};
+
+// K counter workgroups publish; pollers wait for K words (plus any extra
+// ones the test hook asks for, which then never arrive).
+void set_counters(Args& a, int K) {
+  a.K = K;
+  int kp = K + g_extra_counters.load(std::memory_order_relaxed);
+  if (kp > cek::kMaxCounters) kp = cek::kMaxCounters;
+  a.Kpoll = kp;
+}
+
 Args base_args(const void* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V, int64_t ignore,
                void* ws) {
   Args a;
   memset(&a, 0, sizeof(a));
+  const int sl = g_spin_limit.load(std::memory_order_relaxed);
+  a.spin_limit = sl > 0 ? sl : cek::kSpinLimit;
   a.logits = (char*)logits;
   a.ld = ld;
   a.grad = (char*)logits;
@@ -307,7 +324,7 @@ int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int
       fn = f2 ? f2 : ((dtype == CE_DTYPE_BF16) ? aligned_fn<cek::BF16>(c) : aligned_fn<cek::F16>(c));
       G = persistent_grid(fn, c.nt, N);
     }
-    a.K = counters_for(N, G);
+    set_counters(a, counters_for(N, G));
     return launch(fn, G, c.nt, a, st);
   }
   // chunked: per-slab statistics, then merge (+ gradient)
@@ -318,7 +335,7 @@ int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int
   a.C = sp.C;
   const Cfg c = pick_cfg((sp.width + e - 1) / e);
   const int64_t G = N * sp.C;
-  a.K = counters_for(N, G);
+  set_counters(a, counters_for(N, G));
   rc = launch(slab_stats_fn(dtype, c), G, c.nt, a, st);
   if (rc != CE_OK) return rc;
   if (fused && dtype != CE_DTYPE_F32) return launch(slab_grad_fn(dtype, c), G, c.nt, a, st);
@@ -363,13 +380,20 @@ int ce_lin_chunk_f32_to16(const float* logits, int64_t ld, const int64_t* labels
   a.loss_rows = loss_rows;
   a.n_valid_out = n_valid;
   a.status = status;
-  a.K = counters_for(N, N);
+  set_counters(a, counters_for(N, N));
   const Cfg c = pick_cfg((V + 3) / 4);
   KernelFn fn = (out_dtype == CE_DTYPE_BF16) ? f32to16_fn<cek::BF16>(c) : f32to16_fn<cek::F16>(c);
   return launch(fn, N, c.nt, a, st);
 }
 
 int ce_abi_version(void) { return CE_ABI_VERSION; }
+
+int ce_debug_sync_override(int spin_limit, int extra_counters) {
+  if (spin_limit < 0 || extra_counters < 0 || extra_counters > cek::kMaxCounters) return CE_ERR_INVALID_ARG;
+  g_spin_limit.store(spin_limit, std::memory_order_relaxed);
+  g_extra_counters.store(extra_counters, std::memory_order_relaxed);
+  return CE_OK;
+}
 
 const char* ce_error_string(int code) {
   switch (code) {
@@ -436,7 +460,6 @@ int ce_backward(const void* logits, int64_t ld, const int64_t* labels, const dou
     const uintptr_t lend = lo + (uintptr_t)((n_rows - 1) * ld + vocab) * es;
     const uintptr_t gend = go + (uintptr_t)((n_rows - 1) * grad_ld + vocab) * es;
     if (go < lend && lo < gend) return CE_ERR_INVALID_ARG;  // partial overlap
-    if ((go & 15) != (lo & 15) || ((grad_ld * es) & 15) != ((ld * es) & 15)) return CE_ERR_UNSUPPORTED;
   }
   Args a = base_args(logits, ld, labels, n_rows, vocab, ignore_index, nullptr);
   a.grad = (char*)grad;

@@ -64,7 +64,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kStatusLabelRange = 0x1u;
 constexpr uint32_t kStatusSyncTimeout = 0x2u;
 constexpr int kMaxCounters = 64;
-constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus s_sleep): ~0.5 s
+constexpr int kSpinLimit = 1 << 18;  // default polls (each a memory round trip plus s_sleep): ~0.5 s
 
 // ---------------------------------------------------------------------------
 // Workspace header (device memory owned by the caller, zero-filled once).
@@ -369,7 +369,10 @@ struct Args {
   float* slab_xy;    // [N] label logit, written by the slab that holds it
   int64_t chunk;     // slab width in elements (chunked kernels)
   int C;             // slabs per row
-  int K;             // counter workgroups
+  int K;             // counter workgroups (each publishes one partial count)
+  int Kpoll;         // partial-count words a poller waits for (K; more only
+                     // when a host-side test forces the bounded wait to expire)
+  int spin_limit;    // polls before a wait gives up (CE_STATUS_SYNC_TIMEOUT)
 };
 
 // Geometry of V elements starting at `base`: `head` elements before the first
@@ -457,32 +460,36 @@ __device__ __forceinline__ void raise_flag(const Args& a, uint32_t bit) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wave 0 polls the K partial counts and leaves n_valid and the bad-label bit
-// in lds_u[0], lds_u[1] (read them after a barrier).
+// Wave 0 polls the partial counts and leaves n_valid, the bad-label bit and
+// the timeout bit in lds_u[0..2] (read them after a barrier).  A wait that
+// gives up raises CE_STATUS_SYNC_TIMEOUT; the count is then unknown, and the
+// gradient scale of this workgroup becomes NaN (call_scale), so an expired
+// wait can never pass for a valid result.
 __device__ void poll_to_lds(const Args& a, uint32_t tag, uint32_t* lds_u) {
   if ((threadIdx.x >> 6) != 0) return;
   const int lane = threadIdx.x & 63;
   uint64_t w = 0;
   uint32_t to = 0;
-  if (lane < a.K) {
+  if (lane < a.Kpoll) {
     for (int it = 0;; ++it) {
       w = ld_agent(&a.ws->part[lane]);
       if ((uint32_t)(w >> 32) == tag) break;
-      if (it >= kSpinLimit) {
+      if (it >= a.spin_limit) {
         to = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
   }
-  uint32_t c = (lane < a.K) ? (uint32_t)(w & 0x7fffffffu) : 0u;
-  uint32_t b = (lane < a.K) ? (uint32_t)((w >> 31) & 1u) : 0u;
+  uint32_t c = (lane < a.Kpoll) ? (uint32_t)(w & 0x7fffffffu) : 0u;
+  uint32_t b = (lane < a.Kpoll) ? (uint32_t)((w >> 31) & 1u) : 0u;
   c = wave_sum(c);
   b = wave_or(b);
   to = wave_or(to);
   if (lane == 0) {
     lds_u[0] = c;
     lds_u[1] = b;
+    lds_u[2] = to;
     if (to) raise_flag(a, kStatusSyncTimeout);
   }
 }
@@ -503,7 +510,15 @@ __device__ void counts_to_lds(const Args& a, uint32_t* lds_u) {
   if (lane == 0) {
     lds_u[0] = c;
     lds_u[1] = b;
+    lds_u[2] = 0u;
   }
+}
+
+// The gradient scale dloss / n_valid from the count in lds_u (NaN when this
+// workgroup's wait for the count gave up).
+__device__ __forceinline__ double call_scale(const Args& a, const uint32_t* lds_u) {
+  if (lds_u[2]) return __builtin_nan("");
+  return (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
 }
 
 // A row's loss, published for the finisher (one thread).
@@ -513,10 +528,12 @@ __device__ __forceinline__ void publish_loss(const Args& a, int64_t row, float l
 
 // Run by the last workgroup of the grid, after its own row: waits for every
 // row's tagged loss, sums in row order (fp64), writes L, n_valid and status,
-// and bumps the epoch.  n and bad come from this workgroup's poll.
+// and bumps the epoch.  n, bad and the poll's timeout bit come from this
+// workgroup's poll (lds_u[0..2]).  After any expired wait L is NaN.
 template <int NT>
-__device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t bad, double* lds_d) {
+__device__ void finish_call(const Args& a, uint32_t epoch, const uint32_t* lds_u, double* lds_d) {
   const int tid = threadIdx.x;
+  const uint32_t n = lds_u[0], bad = lds_u[1], poll_to = lds_u[2];
   const uint32_t tag = epoch + 1u;
   constexpr int B = 8;  // slot loads in flight per lane
   double acc = 0.0;
@@ -534,7 +551,7 @@ __device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t 
       if (i < a.N) {
         // once one wait has expired the call is already invalid: stop waiting
         for (int it = 0; (uint32_t)(w[j] >> 32) != tag; ++it) {
-          if (to || it >= kSpinLimit) {
+          if (to || it >= a.spin_limit) {
             to = 1;
             break;
           }
@@ -555,7 +572,7 @@ __device__ void finish_call(const Args& a, uint32_t epoch, uint32_t n, uint32_t 
   const int any_to = __syncthreads_or((int)to);
   if (tid == 0) {
     const uint32_t flags = ld_agent(&a.ws->flags) | (any_to ? kStatusSyncTimeout : 0u);
-    a.loss_mean[0] = (float)(lds_d[0] / (double)n);
+    a.loss_mean[0] = (any_to || poll_to) ? __builtin_nanf("") : (float)(lds_d[0] / (double)n);
     a.n_valid_out[0] = (int32_t)n;
     if (a.status) a.status[0] = (bad ? kStatusLabelRange : 0u) | flags;
     st_agent(&a.ws->flags, 0u);
@@ -927,7 +944,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
       if (badlab) {
         nan_row<T, NT, VPL, POL>(gbase, g, tid, 0);
       } else {
-        const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+        const double scale_d = call_scale(a, lds_u);
         const float scale = (float)scale_d;
         const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
         // lower bound of (x - lse) log2e over the row (bf16 lane minima are
@@ -950,7 +967,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
   }
   if (blockIdx.x == gridDim.x - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 
@@ -1057,7 +1074,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_f32_to16_k
       lse = M + logf(S);
       pcomp = S_ex / S;
       loss = (pcomp >= 0.5f) ? (lse - xy) : log1pf(S_ex / ey);
-      const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+      const double scale_d = call_scale(a, lds_u);
       const float scale = (float)scale_d;
       const GradConsts kc = grad_consts<TO>(lse, scale, scale_d, (double)pcomp);
       const float tmin = (MN - lse) * kLog2e;
@@ -1081,7 +1098,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_f32_to16_k
   }
   if (blockIdx.x == gridDim.x - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 
@@ -1212,7 +1229,7 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
         lse = M + logf(S);
         pcomp = S_ex / S;
         loss = (pcomp >= 0.5f) ? (lse - xy) : log1pf(S_ex / ey);
-        const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+        const double scale_d = call_scale(a, lds_u);
         const float scale = (float)scale_d;
         const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
@@ -1233,7 +1250,7 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
   }
   if (blockIdx.x == G - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 
@@ -1311,8 +1328,7 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
       loss = (pcomp >= 0.5) ? (lse - xy) : log1p(S_ex / ey);
     }
     if constexpr (FUSED) {
-      const uint32_t n = lds_u[0];
-      const double scale = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)n;
+      const double scale = call_scale(a, lds_u);
       char* gbase = a.grad + row * a.grad_ld * ESZ;
       u32x4* gbody = (u32x4*)(gbase + g.head * ESZ);
       if (badlab) {
@@ -1352,7 +1368,7 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
   }
   if (blockIdx.x == gridDim.x - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 
@@ -1362,7 +1378,54 @@ __global__ __launch_bounds__(NT) void row_kernel_32(Args a) {
 // blockIdx.x = row * C + slab, a slab being NT*VPL vectors of the row.  16-bit
 // rows take fp64 exponentials only when |s| is large enough for a flushed
 // 2^t to change a rounded output; fp32 rows always compute in fp64.
+//
+// The vectors are those of the gradient row (its 16-byte-aligned body, with
+// head and tail elements before and after it), so every store is a whole
+// aligned vector.  When the logits row has another 16-byte phase than the
+// gradient row (an out-of-place gradient buffer laid out differently), the
+// input of each vector is assembled from the two aligned 16-byte blocks it
+// straddles: both hold at least one byte of the row, and an aligned 16-byte
+// block never crosses a page, so neither load can leave mapped memory; the
+// bytes outside the row are discarded.
 // ---------------------------------------------------------------------------
+// 16 bytes starting r bytes (r in 1..15, even) past the aligned block p.
+template <int POL>
+__device__ __forceinline__ u32x4 ld_shifted(const u32x4* p, uint32_t r) {
+  const u32x4 lo = ldv<POL>(p), hi = ldv<POL>(p + 1);
+  const uint32_t w = r >> 2, b = r & 3u;
+  const uint32_t c[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  uint32_t t[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t c0 = c[i], c1 = c[i + 1], c2 = c[i + 2], c3 = (i + 3 < 8) ? c[i + 3] : 0u;
+    t[i] = (w == 0) ? c0 : (w == 1) ? c1 : (w == 2) ? c2 : c3;
+  }
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_alignbyte(t[d + 1], t[d], b);
+  return o;
+}
+
+template <int NT, int VPL, int POL>
+__device__ __forceinline__ void load_slab(u32x4 (&v)[VPL], const char* in, int nvec, int v0, int tid) {
+  const uint32_t r = (uint32_t)((uintptr_t)in & 15u);
+  if (r == 0) {
+    const u32x4* body = (const u32x4*)in;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = v0 + k * NT + tid;
+      if (idx < nvec) v[k] = ldv<POL>(body + idx);
+    }
+  } else {
+    const u32x4* blk = (const u32x4*)(in - r);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int idx = v0 + k * NT + tid;
+      if (idx < nvec) v[k] = ld_shifted<POL>(blk + idx, r);
+    }
+  }
+}
+
 template <typename T, int NT, int VPL, int POL>
 __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
   constexpr int ESZ = T::ESZ, EPV = T::EPV;
@@ -1373,8 +1436,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
   const int v0 = slab * NT * VPL;
   const char* rbase = a.logits + row * a.ld * ESZ;
   char* gbase = a.grad + row * a.grad_ld * ESZ;
-  const Geom g = geom<ESZ, EPV>(rbase, a.V);
-  const u32x4* body = (const u32x4*)(rbase + g.head * ESZ);
+  const Geom g = geom<ESZ, EPV>(gbase, a.V);  // the gradient row's vectors
   u32x4* gbody = (u32x4*)(gbase + g.head * ESZ);
   const int64_t y = a.labels[row];
   if (y == a.ignore) {
@@ -1390,11 +1452,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
   const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)a.n_valid_in[0];
   const double gy_d = -scale_d * a.pcomp_in[row];
   u32x4 v[VPL];
-#pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int idx = v0 + k * NT + tid;
-    if (idx < g.nvec) v[k] = ldv<POL>(body + idx);
-  }
+  load_slab<NT, VPL, POL>(v, rbase + g.head * ESZ, g.nvec, v0, tid);
   if constexpr (ESZ == 2) {
     const bool hh = slab == 0 && tid < g.head, ht = slab == 0 && tid < g.tail;
     const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
@@ -1428,11 +1486,12 @@ __global__ __launch_bounds__(NT) void grad_kernel(Args a) {
       }
     }
     float* grow = (float*)gbase;
+    const float* xrow = (const float*)rbase;
     if (slab == 0) {
-      if (tid < g.head) grow[tid] = (float)(exp_f64((double)((const float*)rbase)[tid] - lse_d) * scale_d);
+      if (tid < g.head) grow[tid] = (float)(exp_f64((double)xrow[tid] - lse_d) * scale_d);
       if (tid < g.tail) {
         const int64_t j = g.head + (int64_t)g.nvec * EPV + tid;
-        grow[j] = (float)(exp_f64((double)((const float*)rbase)[j] - lse_d) * scale_d);
+        grow[j] = (float)(exp_f64((double)xrow[j] - lse_d) * scale_d);
       }
     }
     // the label's gradient overwrites the value this lane just stored for it
@@ -1578,7 +1637,7 @@ __global__ __launch_bounds__(NT) void slab_merge_kernel(Args a) {
   }
   if (blockIdx.x == gridDim.x - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 
@@ -1632,7 +1691,7 @@ __global__ __launch_bounds__(NT, 4) void slab_grad_kernel(Args a) {
     if (badlab) {
       nan_row<T, NT, VPL, POL>(sbase, g, tid, 0);
     } else {
-      const double scale_d = (a.dloss ? (double)a.dloss[0] : 1.0) / (double)lds_u[0];
+      const double scale_d = call_scale(a, lds_u);
       const float scale = (float)scale_d, lse = (float)lds_r[0];
       const bool hh = tid < g.head, ht = tid < g.tail;
       const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
@@ -1661,7 +1720,7 @@ __global__ __launch_bounds__(NT, 4) void slab_grad_kernel(Args a) {
   }
   if (blockIdx.x == gridDim.x - 1) {
     __syncthreads();
-    finish_call<NT>(a, epoch, lds_u[0], lds_u[1], lds_d);
+    finish_call<NT>(a, epoch, lds_u, lds_d);
   }
 }
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 4
+#define CE_ABI_VERSION 5
 
 /* element formats of logits and gradients */
 enum ce_dtype { CE_DTYPE_F32 = 0, CE_DTYPE_BF16 = 1, CE_DTYPE_F16 = 2 };
@@ -82,6 +82,23 @@ enum ce_error {
 
 /* ABI version of the loaded library (CE_ABI_VERSION it was built with). */
 int ce_abi_version(void);
+
+/*
+ * Test hook for the bounded inter-workgroup wait of the token mean (the mean
+ * over valid tokens, fms-hf-tuning PR #280, "Early Version Of This Plugin",
+ * needs the batch's valid-token count before any gradient is scaled, so the
+ * single-launch kernels wait for partial counts published by other
+ * workgroups).  spin_limit > 0 replaces the default number of polls before a
+ * wait gives up (0 restores it); extra_counters > 0 makes every poller also
+ * wait for that many partial-count words that no workgroup publishes, so each
+ * wait expires after spin_limit polls and every workgroup still exits.  A call
+ * whose wait expired reports CE_STATUS_SYNC_TIMEOUT, writes NaN to loss_mean
+ * and NaN gradients for its valid rows; ce_workspace_init then makes the
+ * workspace ready again.  Process-wide; affects launches made after it
+ * returns.  Returns CE_ERR_INVALID_ARG for negative values or
+ * extra_counters > 64.
+ */
+int ce_debug_sync_override(int spin_limit, int extra_counters);
 
 /* Static text for a return code or status bit. */
 const char* ce_error_string(int code);
@@ -140,10 +157,11 @@ int ce_forward(const void* logits, int64_t ld, const int64_t* labels, int64_t n_
  *   n_valid   device int32 from the forward.
  *   grad      n_rows rows of `vocab` elements of dtype, row i at i * grad_ld.
  *             May be the logits buffer itself (in place, grad_ld == ld); if it
- *             is a different buffer it must not overlap logits and must share
- *             the logits' 16-byte alignment (grad % 16 == logits % 16 and
- *             grad_ld * esize % 16 == ld * esize % 16), else
- *             CE_ERR_UNSUPPORTED.
+ *             is a different buffer it must not overlap logits
+ *             (CE_ERR_INVALID_ARG).  Its alignment and stride are free (element
+ *             aligned): the kernel writes whole 16-byte vectors of the
+ *             gradient rows and assembles each vector's logits from the
+ *             16-byte blocks they straddle when the two layouts differ.
  */
 int ce_backward(const void* logits, int64_t ld, const int64_t* labels, const double* lse_rows,
                 const double* pcomp_rows, const int32_t* n_valid, const float* dloss,

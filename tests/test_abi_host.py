@@ -120,12 +120,18 @@ def backward(lib, logits=FAKE, ld=100, labels=FAKE, lse=FAKE, pcomp=FAKE, n_vali
     (dict(grad_ld=99), _lib.CE_ERR_INVALID_ARG),
     (dict(grad_ld=104), _lib.CE_ERR_INVALID_ARG),            # in place needs the same stride
     (dict(grad=FAKE + 64), _lib.CE_ERR_INVALID_ARG),         # partial overlap with the logits
-    (dict(grad=FAKE + 4096 + 2), _lib.CE_ERR_UNSUPPORTED),   # different 16-byte phase
-    (dict(grad=FAKE + 4096, grad_ld=101), _lib.CE_ERR_UNSUPPORTED),
+    (dict(grad=FAKE + 4096 + 2, lse=0), _lib.CE_ERR_INVALID_ARG),  # another layout is served; NULL lse is not
     (dict(grad=FAKE + 4097), _lib.CE_ERR_INVALID_ARG),       # not element aligned
 ])
 def test_backward_rejects(lib, kw, code):
     assert backward(lib, **kw) == code
+
+
+def test_sync_override_rejects(lib):
+    assert lib.ce_debug_sync_override(-1, 0) == _lib.CE_ERR_INVALID_ARG
+    assert lib.ce_debug_sync_override(0, -1) == _lib.CE_ERR_INVALID_ARG
+    assert lib.ce_debug_sync_override(0, 65) == _lib.CE_ERR_INVALID_ARG
+    assert lib.ce_debug_sync_override(0, 0) == _lib.CE_OK
 
 
 def test_workspace_init_rejects(lib):
