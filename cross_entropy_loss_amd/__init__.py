@@ -21,7 +21,7 @@ from ._lib import (CE_STATUS_LABEL_RANGE, CE_STATUS_SYNC_TIMEOUT, CeError)  # no
 
 __all__ = [
     "ce_workspace_bytes", "ce_workspace_init", "Workspace", "ce_forward", "ce_backward",
-    "ce_fwd_bwd_inplace", "cross_entropy", "FastCrossEntropyLoss", "CeError",
+    "ce_fwd_bwd_inplace", "ce_fwd_bwd_inplace_noalloc", "cross_entropy", "FastCrossEntropyLoss", "CeError",
     "ce_linear_workspace_bytes", "ce_linear_fwd_bwd", "ce_rmsnorm_workspace_bytes", "ce_rmsnorm_forward",
     "ce_rmsnorm_backward", "rms_norm", "FastRMSNorm", "ce_rope", "rope", "FastRoPE",
 ]
@@ -185,6 +185,24 @@ def ce_fwd_bwd_inplace(logits: torch.Tensor, labels: torch.Tensor, ignore_index:
         _ptr(out["loss_rows"]), _ptr(out["lse_rows"]), _ptr(out["pcomp_rows"]), _ptr(out["n_valid"]),
         _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(logits.device))
     _lib.check(rc, "ce_fwd_bwd_inplace")
+    return out
+
+
+def ce_fwd_bwd_inplace_noalloc(logits: torch.Tensor, labels: torch.Tensor, out: dict, ignore_index: int = -100,
+                               chunk: int = 0, dloss: torch.Tensor | None = None) -> dict:
+    """ce_fwd_bwd_inplace on the library's static per-GPU scratch: no
+    workspace, and nothing allocated here either (the caller passes `out`,
+    as made by _outputs(rows, device)).  Calls on one GPU must be ordered."""
+    N, V, ld = _rows(logits)
+    dt = _dtype_code(logits)
+    labels = _labels(labels, N, logits.device)
+    if dloss is not None and (dloss.dtype != torch.float32 or dloss.numel() != 1):
+        raise ValueError("dloss must be a one-element float32 tensor")
+    rc = _lib.load().ce_fwd_bwd_inplace_noalloc(
+        _ptr(logits), ld, _ptr(labels), N, V, dt, ignore_index, chunk, _ptr(dloss), _ptr(out["loss_mean"]),
+        _ptr(out["loss_rows"]), _ptr(out["lse_rows"]), _ptr(out["pcomp_rows"]), _ptr(out["n_valid"]),
+        _ptr(out["status"]), _stream(logits.device))
+    _lib.check(rc, "ce_fwd_bwd_inplace_noalloc")
     return out
 
 

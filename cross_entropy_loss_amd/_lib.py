@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libce_mi355x.so")
 
 CE_DTYPE_F32, CE_DTYPE_BF16, CE_DTYPE_F16 = 0, 1, 2
-CE_OK, CE_ERR_INVALID_ARG, CE_ERR_DTYPE, CE_ERR_WORKSPACE, CE_ERR_UNSUPPORTED, CE_ERR_HIP = range(6)
+CE_OK, CE_ERR_INVALID_ARG, CE_ERR_DTYPE, CE_ERR_WORKSPACE, CE_ERR_UNSUPPORTED, CE_ERR_HIP, CE_ERR_SCRATCH = range(7)
 CE_STATUS_LABEL_RANGE = 0x1
 CE_STATUS_SYNC_TIMEOUT = 0x2
 ABI_VERSION = 5
@@ -29,6 +29,8 @@ SIGNATURES = {
     "ce_backward": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _i64, _vp, _i64, _vp], _int),
     "ce_fwd_bwd_inplace": ([_vp, _i64, _vp, _i64, _i64, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                             _sz, _vp], _int),
+    "ce_fwd_bwd_inplace_noalloc": ([_vp, _i64, _vp, _i64, _i64, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp], _int),
     "ce_linear_workspace_bytes": ([_i64, _i64, _i64, _i64, _int], _sz),
     "ce_rmsnorm_workspace_bytes": ([_i64, _i64, _int], _sz),
     "ce_rmsnorm_forward": ([_vp, _i64, _vp, _i64, _i64, _int, ctypes.c_float, _vp, _i64, _vp, _vp], _int),

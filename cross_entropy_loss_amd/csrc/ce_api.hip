@@ -353,9 +353,61 @@ int run_forward(bool fused, void* logits, int64_t ld, const int64_t* labels, int
   return launch(grad_fn(dtype), N * (int64_t)b.C, kGradNT, b, st);
 }
 
+// ---- the allocation-free entry point ---------------------------------------
+// Its workspace is this file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is a stand-in symbol, not a device address): the device
+// address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept below.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  int rc = CE_ERR_HIP;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address; on first use on a device, the lookup
+// and a zero fill enqueued on `st` (the workspace protocol starts from zero).
+int device_scratch(hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CE_ERR_HIP;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return;
+    hipLaunchKernelGGL(cek::ws_fill_kernel, dim3(256), dim3(256), 0, st, (uint32_t*)p, kScratchBytes / 4);
+    if (hipGetLastError() != hipSuccess) return;
+    sl.ptr = p;
+    sl.rc = CE_OK;
+  });
+  *out = sl.ptr;
+  return sl.rc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, int64_t n_rows, int64_t vocab,
+                               int dtype, int64_t ignore_index, int64_t chunk, const float* dloss, float* loss_mean,
+                               float* loss_rows, double* lse_rows, double* pcomp_rows, int32_t* n_valid,
+                               uint32_t* status, void* stream) {
+  int rc = check_shape(logits, ld, labels, n_rows, vocab, dtype);
+  if (rc != CE_OK) return rc;
+  if (chunk < 0) return CE_ERR_INVALID_ARG;
+  Split sp;
+  if (!make_split(vocab, chunk, dtype, &sp)) return CE_ERR_UNSUPPORTED;
+  if (ws_layout(n_rows, sp).total > kScratchBytes) return CE_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = device_scratch((hipStream_t)stream, &ws);
+  if (rc != CE_OK) return rc;
+  return run_forward(true, logits, ld, labels, n_rows, vocab, dtype, ignore_index, chunk, dloss, loss_mean,
+                     loss_rows, lse_rows, pcomp_rows, n_valid, status, ws, kScratchBytes, (hipStream_t)stream);
+}
 
 int ce_lin_chunk_f32_to16(const float* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V,
                           int out_dtype, int64_t ignore_index, const float* dloss, float* loss_mean, float* loss_rows,
@@ -403,6 +455,7 @@ const char* ce_error_string(int code) {
     case CE_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than ce_workspace_bytes()";
     case CE_ERR_UNSUPPORTED: return "request not served by this library";
     case CE_ERR_HIP: return "HIP runtime error";
+    case CE_ERR_SCRATCH: return "request needs more than the allocation-free entry point's 8 MiB static scratch";
     default: return "unknown error code";
   }
 }

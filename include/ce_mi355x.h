@@ -73,7 +73,8 @@ enum ce_error {
   CE_ERR_DTYPE = 2,       /* unknown dtype */
   CE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than ce_workspace_bytes() */
   CE_ERR_UNSUPPORTED = 4, /* a valid request this library does not serve */
-  CE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+  CE_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+  CE_ERR_SCRATCH = 6      /* more workspace than ce_fwd_bwd_inplace_noalloc's static scratch */
 };
 
 /* bits OR-ed into the status word by the kernels */
@@ -180,6 +181,25 @@ int ce_fwd_bwd_inplace(void* logits, int64_t ld, const int64_t* labels, int64_t 
                        const float* dloss, float* loss_mean, float* loss_rows, double* lse_rows,
                        double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * ce_fwd_bwd_inplace without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * ce_fwd_bwd_inplace; its workspace is a static device array of 8 MiB per GPU
+ * inside the library (enough for n_rows up to about one million unchunked
+ * rows: header 1 KiB + 8 bytes per row, plus the slab partials of rows wider
+ * than on-chip capacity), looked up and zero-filled on `stream` on the first
+ * call on each device and held until the process ends.  Calls no allocating
+ * routine.  Requests whose ce_workspace_bytes() exceeds 8 MiB return
+ * CE_ERR_SCRATCH before anything is enqueued.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (unordered streams,
+ * concurrent host threads without ordering) race and must be avoided.
+ */
+int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, int64_t n_rows,
+                               int64_t vocab, int dtype, int64_t ignore_index, int64_t chunk,
+                               const float* dloss, float* loss_mean, float* loss_rows, double* lse_rows,
+                               double* pcomp_rows, int32_t* n_valid, uint32_t* status, void* stream);
 
 /*
  * LM-head projection followed by the cross-entropy above, forward and

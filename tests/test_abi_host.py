@@ -134,6 +134,16 @@ def test_sync_override_rejects(lib):
     assert lib.ce_debug_sync_override(0, 0) == _lib.CE_OK
 
 
+def test_noalloc_rejects_oversized_request(lib):
+    # 2^21 rows need 16 MiB of tagged loss slots: more than the static scratch
+    f = VP(FAKE)
+    assert lib.ce_fwd_bwd_inplace_noalloc(f, 100, f, 1 << 21, 100, 1, -100, 0, None, f, f, f, f, f, f,
+                                          None) == _lib.CE_ERR_SCRATCH
+    # argument errors come first
+    assert lib.ce_fwd_bwd_inplace_noalloc(f, 99, f, 4, 100, 1, -100, 0, None, f, f, f, f, f, f,
+                                          None) == _lib.CE_ERR_INVALID_ARG
+
+
 def test_workspace_init_rejects(lib):
     assert lib.ce_workspace_init(None, 4096, None) == _lib.CE_ERR_WORKSPACE
     assert lib.ce_workspace_init(VP(FAKE), 100, None) == _lib.CE_ERR_WORKSPACE
