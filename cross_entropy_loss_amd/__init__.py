@@ -243,6 +243,11 @@ def ce_linear_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
         "grad_weight": torch.empty_like(weight, memory_format=torch.contiguous_format) if want_grad_weight else None,
     }
     gh, gw = out["grad_hidden"], out["grad_weight"]
+    if workspace is None:  # its own: the cross-entropy workspaces carry their own state from call to call
+        key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+        workspace = _lin_ws.get(key)
+        if workspace is None:
+            workspace = _lin_ws[key] = Workspace(dev)
     ws = _workspace(dev, ce_linear_workspace_bytes(N, H, V, chunk_rows, hidden.dtype), workspace)
     rc = _lib.load().ce_linear_fwd_bwd(
         _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(labels), N, H, V, dt, ignore_index, chunk_rows, _ptr(dloss),
@@ -254,6 +259,7 @@ def ce_linear_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
 
 
 _norm_ws: dict = {}
+_lin_ws: dict = {}
 
 
 def ce_rmsnorm_workspace_bytes(n_rows: int, hidden: int, dtype: torch.dtype) -> int:

@@ -1,6 +1,6 @@
-// ce_linear.hip -- LM-head projection followed by the cross-entropy of
-// ce_api.hip, forward and backward, token-chunked (the C ABI in
-// include/ce_mi355x.h: ce_linear_workspace_bytes, ce_linear_fwd_bwd).
+// ce_linear.hip -- LM-head projection followed by the token-mean softmax
+// cross-entropy, forward and backward (the C ABI in include/ce_mi355x.h:
+// ce_linear_workspace_bytes, ce_linear_fwd_bwd).
 //
 // The pages compare the plain cross-entropy kernel with a fused linear
 // cross-entropy (PyPI page "fms-acceleration-foak 0.7.4", "Running Liger
@@ -10,128 +10,164 @@
 // the weight W [V, H] of a bias-free linear layer, logits = h W^T, and
 //   dL/dh = g W,   dL/dW = g^T h,   g = dloss * dL/dlogits.
 //
-// Per chunk of T rows, on the caller's stream:
-//   1. logits_c = h_c W^T            rocBLAS GEMM, fp32 accumulate, fp32 out
-//   2. loss and g over logits_c      ce_fwd_bwd_inplace on the fp32 chunk, its
-//                                    dloss set to dloss * n_c / n so that its
-//                                    scale dloss' / n_c is the batch's dloss / n
-//   3. g rounded to the input format (bf16 / fp16) for the two GEMMs below
-//   4. dh_c = g W                    rocBLAS GEMM, fp32 accumulate, dtype out
-//   5. dW32 += g^T h_c               GEMM, fp32 accumulate and out (16-bit, shapes
-//                                    tiling by 64: TN on transposed copies of g, h_c)
-// then dW32 is rounded once to the input format (with a single chunk the GEMM
-// writes the input format itself, from its fp32 sums), and the token mean over the
-// whole batch is summed in row order in fp64.  The batch's logits are never
-// stored: one fp32 chunk (T x V) lives in the workspace.
+// bf16 / fp16 (all three products on the matrix cores, lin_gemm.h):
+//   1. prep: n_valid, the gradient scale s = dloss 2^k / n_valid (fp16 keeps
+//      g in its normal range through 2^k, k = 14 - ilogb(dloss / n); bf16
+//      k = 0), and a new epoch tag for the call.
+//   2. logits + cross-entropy, cooperative, in chunks of rows: each
+//      workgroup holds one 256 x 256 logits tile in its fp32 accumulators, so
+//      no logits ever reach memory.  From the registers it takes per row the
+//      tile's (max, sum of exp without the label column), publishes them as
+//      epoch-tagged words, merges the rows it owns (every tile of a row is
+//      resident at once: the chunk's grid is sized to be co-resident and
+//      launched cooperatively), publishes lse and 1 - p_y, and then writes
+//      the gradient tile g = s (softmax - onehot) in the input format straight
+//      from its accumulators -- the per-chunk log-sum-exp merge of a chunked
+//      loss, done across workgroups.
+//   3. dh = g W        MFMA, g K-contiguous, W read K-outer (transposed on its
+//                      way into LDS); scaled by 2^-k on output
+//   4. dW = g^T h      MFMA, both read K-outer; scaled by 2^-k on output
+//   5. the token mean over the batch, summed in row order in fp64.
+// The workspace holds g (N x V in the input format) and the small tagged
+// exchange arrays; no fp32 logits and no transposed copies.
 //
-// fp16 range.  |g| <= s = dloss / n (about 1e-6 at n = 4096 and V = 32000
-// per element), deep in fp16's subnormal range, where rounding g for the
-// GEMMs would cost percents.  For fp16 the chunk's dloss' carries a power of
-// two 2^k, k = 14 - ilogb(s), so the rounded g lies below 2^15 and keeps its
-// 11 bits down to s 2^-28; the dh GEMM takes alpha = 2^-k and the final dW
-// cast multiplies by 2^-k, both exact.  bf16 and fp32 have fp32's range and
-// keep k = 0.
+// fp32 inputs: the same steps with a plain tiled fp32 GEMM (no MFMA) and the
+// chunk's fp32 logits in the workspace, reduced by the cross-entropy kernels
+// of ce_api.hip in place; dW accumulates in the output.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
 #include <math.h>
-#include <rocblas/rocblas.h>
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
-#include <vector>
-
 #include "ce_internal.h"
 #include "ce_mi355x.h"
+#include "lin_gemm.h"
 
 namespace {
 
-// 4096 rows: the chunk's fp32 logits and rounded gradient take 4096 V 6
-// bytes (786 MB at V = 32000), and the GEMMs run at their larger-shape
-// rate (4096 x 4096 x 32000 bf16: 3.7 ms per call against 5.5 ms with
-// 1024-row chunks).
-constexpr int64_t kDefaultChunkRows = 4096;
-constexpr int64_t kMaxChunks = 4096;  // per-chunk counts live in LDS
-constexpr int kNT = 1024;
+using lg::f32x16;
+using lg::Tile;
+
+constexpr int kNT = 1024;               // prep / finish kernels
+constexpr int64_t kMaxChunks = 4096;    // per-chunk counts live in LDS (fp32 path)
+constexpr int64_t kF32ChunkRows = 1024;  // fp32 path default
+constexpr int kSpinLimit = 1 << 20;      // polls before an exchange wait gives up
+constexpr uint32_t kStatusLabelRange = 0x1u, kStatusSyncTimeout = 0x2u;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int dtype) { return dtype == CE_DTYPE_F32 ? 4 : 2; }
 bool valid_dtype(int d) { return d == CE_DTYPE_F32 || d == CE_DTYPE_BF16 || d == CE_DTYPE_F16; }
+bool fits32(int64_t x) { return x >= 0 && x < ((int64_t)1 << 31); }
 
-// Rows per chunk: a multiple of 64 (a wave's labels fall in one chunk) and
-// at most kMaxChunks chunks.
-int64_t chunk_rows_for(int64_t N, int64_t chunk_rows) {
-  int64_t t = chunk_rows > 0 ? chunk_rows : kDefaultChunkRows;
-  const int64_t min_t = (N + kMaxChunks - 1) / kMaxChunks;
-  if (t < min_t) t = min_t;
-  t = (t + 63) / 64 * 64;
-  return t;
-}
+// ---------------------------------------------------------------------------
+// Workspace of the 16-bit path.
+// ---------------------------------------------------------------------------
+struct LinHeader {
+  uint32_t epoch;   // bumped by prep: this call's tag
+  uint32_t status;  // status bits of this call (cleared by prep)
+  float gscale;     // s = dloss 2^k / n_valid
+  float unscale;    // 2^-k
+  int32_t n_valid;
+  uint32_t pad[59];
+};
+static_assert(sizeof(LinHeader) == 256, "header size");
 
-struct LinLayout {
-  size_t ce_ws, logits, g16, dw32, dl_chunk, chunk_status, chunk_loss, chunk_n, consts, gT, hT, total;
-  bool tn;  // weight gradient from transposed operands
-  size_t ce_ws_bytes;
-  int64_t T;
-  int nc;
+struct FastLayout {
+  size_t g, stats, xy, lse, pc, total;
+  int64_t ldg;    // g's row stride: vocab rounded up to 8 elements
+  int nvt;        // vocabulary tiles of 256
+  int rt_chunk;   // row tiles per chunk
+  int nchunks;
 };
 
-LinLayout lin_layout(int64_t N, int64_t H, int64_t V, int64_t chunk_rows, int dtype) {
-  LinLayout L;
+// Row tiles per cooperative chunk: every tile of the chunk resident at once.
+FastLayout fast_layout(int64_t N, int64_t V, int64_t resident) {
+  FastLayout L;
   memset(&L, 0, sizeof(L));
-  L.T = chunk_rows_for(N, chunk_rows);
-  L.nc = (int)((N + L.T - 1) / L.T);
-  const int64_t Tc = (N < L.T) ? (N > 0 ? N : 1) : L.T;
-  L.ce_ws_bytes = ce_workspace_bytes(Tc, V, 0, CE_DTYPE_F32);
-  size_t off = 0;
-  L.ce_ws = off;
-  off += align256(L.ce_ws_bytes);
-  L.logits = off;
-  off += align256((size_t)Tc * V * 4);
-  if (dtype != CE_DTYPE_F32) {
-    L.g16 = off;
-    off += align256((size_t)Tc * V * 2);
-    if (L.nc > 1) {  // one chunk: the weight-gradient GEMM writes the output format directly
-      L.dw32 = off;
-      off += align256((size_t)V * H * 4);
-    }
-  }
-  const size_t nc = (size_t)(L.nc > 0 ? L.nc : 1);
-  L.dl_chunk = off;
-  off += align256(nc * 4);
-  L.chunk_status = off;
-  off += align256(nc * 4);
-  L.chunk_loss = off;
-  off += align256(nc * 4);
-  L.chunk_n = off;
-  off += align256(nc * 4);
-  L.consts = off;  // 1, 0, 2^-k (GEMM scalars read in device pointer mode)
-  off += 256;
-  // 16-bit weight gradient as a TN GEMM on transposed copies of the chunk's
-  // g and h (reduction dimension contiguous: 0.81 vs 1.03 ms for the NT form
-  // on 4096 x 4096 x 32000 bf16), when every chunk tiles by 64
-  // (T is a multiple of 64, so N % 64 == 0 makes every chunk's rows one)
-  L.tn = dtype != CE_DTYPE_F32 && N > 0 && N % 64 == 0 && V % 64 == 0 && H % 64 == 0;
-  if (L.tn) {
-    L.gT = off;
-    off += align256((size_t)V * Tc * 2);
-    L.hT = off;
-    off += align256((size_t)H * Tc * 2);
-  }
+  L.ldg = (V + 7) / 8 * 8;
+  L.nvt = (int)((V + 255) / 256);
+  const int64_t rt_total = (N + 255) / 256;
+  int64_t rc = resident / L.nvt;
+  if (rc < 1) rc = 1;
+  if (rc > rt_total) rc = rt_total > 0 ? rt_total : 1;
+  L.rt_chunk = (int)rc;
+  L.nchunks = (int)((rt_total + rc - 1) / rc);
+  size_t off = sizeof(LinHeader);
+  L.g = align256(off);
+  off = L.g + align256((size_t)N * L.ldg * 2);
+  L.stats = off;  // [chunk][row in chunk][vocab tile] x 2 tagged words
+  off += align256((size_t)(L.nchunks > 0 ? L.nchunks : 1) * rc * 256 * L.nvt * 16);
+  L.xy = off;
+  off += align256((size_t)N * 8);
+  L.lse = off;
+  off += align256((size_t)N * 8);
+  L.pc = off;
+  off += align256((size_t)N * 8);
   L.total = off;
   return L;
 }
 
-// ---------------------------------------------------------------------------
-// Kernels.
-// ---------------------------------------------------------------------------
+// Co-resident workgroups of the 16-bit logits kernel: one per CU (its LDS
+// and accumulator registers fill a CU).  Taken as the device's CU count.
+int64_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
 
-// One workgroup: valid rows per chunk (T a multiple of 64, so a wave's 64
-// consecutive labels fall in one chunk), the batch count n, each chunk's
-// dloss' = dloss 2^k n_c / n, and the GEMM scalars {1, 0, 2^-k}.
+// ---------------------------------------------------------------------------
+// Tagged exchange words: tag << 32 | float bits, one relaxed agent-scope
+// 64-bit store / load each (the reader polls until the tag is this call's).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// Polls *p until it carries `tag`; on timeout returns NaN and sets *to.
+__device__ __forceinline__ float get_tagged(const uint64_t* p, uint32_t tag, uint32_t& to) {
+  for (int it = 0;; ++it) {
+    const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == tag) return __builtin_bit_cast(float, (uint32_t)w);
+    if (to || it >= kSpinLimit) {
+      to = 1;
+      return __builtin_nanf("");
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t to_bits(float x);
+template <>
+__device__ __forceinline__ uint16_t to_bits<__bf16>(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <>
+__device__ __forceinline__ uint16_t to_bits<_Float16>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// 1. prep (one workgroup): n_valid, the scale, the epoch; for the fp32 path
+// also each chunk's dloss share.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, int64_t N, int64_t ignore, int64_t T,
-                                                       int nc, const float* dloss, int fp16_range, float* dl_chunk,
-                                                       int32_t* n_valid_out, float* consts) {
+                                                       int nc, const float* dloss, int fp16_range, LinHeader* hdr,
+                                                       float* dl_chunk, int32_t* n_valid_out) {
   __shared__ int32_t cnt[kMaxChunks];
   __shared__ int64_t wsum[kNT / 64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -141,11 +177,13 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
     const int64_t i = base + tid;
     const bool v = i < N && labels[i] != ignore;
     const uint64_t ballot = __ballot(v);
-    if (lane == 0 && ballot) atomicAdd(&cnt[(int)((i) / T)], (int32_t)__popcll(ballot));
+    // T is a multiple of 64: a wave's labels fall in one chunk
+    if (lane == 0 && ballot && dl_chunk) atomicAdd(&cnt[(int)(i / T)], (int32_t)__popcll(ballot));
+    if (lane == 0 && ballot && !dl_chunk) atomicAdd(&cnt[0], (int32_t)__popcll(ballot));
   }
   __syncthreads();
   int64_t s = 0;
-  for (int c = tid; c < nc; c += kNT) s += cnt[c];
+  for (int c = tid; c < (dl_chunk ? nc : 1); c += kNT) s += cnt[c];
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
   if (lane == 0) wsum[tid >> 6] = s;
   __syncthreads();
@@ -161,39 +199,293 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
     }
   }
   const double up = ldexp(1.0, k);
-  for (int c = tid; c < nc; c += kNT) dl_chunk[c] = n > 0 ? (float)(dl * up * (double)cnt[c] / (double)n) : 0.0f;
+  if (dl_chunk)
+    for (int c = tid; c < nc; c += kNT) dl_chunk[c] = n > 0 ? (float)(dl * up * (double)cnt[c] / (double)n) : 0.0f;
   if (tid == 0) {
     n_valid_out[0] = (int32_t)n;
-    consts[0] = 1.0f;
-    consts[1] = 0.0f;
-    consts[2] = (float)ldexp(1.0, -k);
-  }
-}
-
-// fp32 * scale (a power of two, or NULL = 1) -> storage format, nearest-even,
-// one workgroup per row: 16-byte loads and 8-byte stores where the row's
-// alignment allows (a per-row choice), single elements otherwise.
-template <typename T>
-__global__ __launch_bounds__(256) void lin_cast_kernel(const float* src, int64_t ld_src, int64_t cols, T* dst,
-                                                       int64_t ld_dst, const float* scale) {
-  const float* s = src + (int64_t)blockIdx.x * ld_src;
-  T* d = dst + (int64_t)blockIdx.x * ld_dst;
-  const float f = scale ? scale[0] : 1.0f;
-  int64_t j0 = 0;
-  if ((uintptr_t)s % 16 == 0 && (uintptr_t)d % 8 == 0) {
-    const int64_t n4 = cols / 4;
-    for (int64_t q = threadIdx.x; q < n4; q += 256) {
-      const float4 x = ((const float4*)s)[q];
-      const T o[4] = {(T)(x.x * f), (T)(x.y * f), (T)(x.z * f), (T)(x.w * f)};
-      uint2 w;
-      __builtin_memcpy(&w, o, sizeof(w));
-      ((uint2*)d)[q] = w;
+    if (hdr) {
+      hdr->epoch = hdr->epoch + 1u;
+      hdr->status = 0u;
+      hdr->gscale = n > 0 ? (float)(dl * up / (double)n) : 0.0f;
+      hdr->unscale = (float)ldexp(1.0, -k);
+      hdr->n_valid = (int32_t)n;
     }
-    j0 = n4 * 4;
   }
-  for (int64_t j = j0 + threadIdx.x; j < cols; j += 256) d[j] = (T)(s[j] * f);
 }
 
+// ---------------------------------------------------------------------------
+// 2. logits tile + cross-entropy epilogue (16-bit; cooperative launch per
+// chunk of row tiles).  Grid: rt_chunk x nvt workgroups; blockIdx.x = vt *
+// rtc + rt, so the row tiles that share a weight slab run side by side.
+// ---------------------------------------------------------------------------
+struct LogitsArgs {
+  const char* h;
+  int64_t ldh;
+  const char* w;
+  int64_t ldw;
+  const int64_t* labels;
+  int64_t ignore;
+  int64_t N, H, V;
+  int64_t row0;  // first row of this chunk
+  int rtc;       // row tiles in this chunk
+  int nvt;
+  LinHeader* hdr;
+  uint16_t* g;
+  int64_t ldg;
+  uint64_t* stats;  // this chunk's [rtc * 256][nvt][2]
+  uint64_t* xy;     // [N]
+  uint64_t* lse;    // [N]
+  uint64_t* pc;     // [N]
+  float* loss_rows;
+};
+
+template <typename T, bool DMA, int AK, int BKD>
+__global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int rt = (int)(blockIdx.x % a.rtc), vt = (int)(blockIdx.x / a.rtc);
+  const int64_t mrow0 = a.row0 + (int64_t)rt * 256;  // the tile's first row (global)
+  const int n0 = vt * 256;
+  const int M = (int)a.N, Nv = (int)a.V, K = (int)a.H;
+  Tile t;
+  if constexpr (DMA) lg::tile_nt<T>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
+  else lg::tile_rs<T, AK, BKD>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
+  const uint32_t tag = a.hdr->epoch;
+  const float gs = a.hdr->gscale;
+  __syncthreads();  // every wave is done with the K loop's LDS
+
+  int64_t* ys = (int64_t*)lds;              // [256] labels of the tile's rows
+  float* red = (float*)(lds + 2048);         // [2 waves][256 rows][2]
+  float* pm = (float*)(lds + 6144);         // merge inputs: [<= 512][2]
+  float* lrow = (float*)(lds + 10240);      // [256] lse of the tile's rows
+  float* prow = (float*)(lds + 11264);      // [256] 1 - p_y
+  uint32_t* sflag = (uint32_t*)(lds + 12288);
+  if (tid == 0) sflag[0] = 0u;
+  {
+    const int64_t R = mrow0 + tid;
+    ys[tid] = (R < a.N) ? a.labels[R] : a.ignore;
+  }
+  __syncthreads();
+
+  // the tile's per-row (max, label-excluded sum), this wave's 128 columns
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = lg::acc_row(wm, i, v, lane);
+      const int64_t y = ys[r];
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = n0 + lg::acc_col(wn, j, lane);
+        if (c < Nv) m = fmaxf(m, t.acc[i][j][v]);
+      }
+      m = half_max(m);
+      float s = 0.0f;
+      const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = n0 + lg::acc_col(wn, j, lane);
+        const float x = t.acc[i][j][v];
+        if (c < Nv && (int64_t)c != y) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mc));
+        if ((int64_t)c == y && mrow0 + r < a.N) put_tagged(a.xy + mrow0 + r, tag, x);
+      }
+      s = half_sum(s);
+      if ((lane & 31) == 0) {
+        red[(wn * 256 + r) * 2] = m;
+        red[(wn * 256 + r) * 2 + 1] = s;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int r = tid;
+    const float m0 = red[r * 2], s0 = red[r * 2 + 1], m1 = red[(256 + r) * 2], s1 = red[(256 + r) * 2 + 1];
+    const float Mx = fmaxf(m0, m1);
+    const float S = ((m0 == -INFINITY) ? 0.0f : s0 * __builtin_amdgcn_exp2f((m0 - Mx) * kLog2e)) +
+                    ((m1 == -INFINITY) ? 0.0f : s1 * __builtin_amdgcn_exp2f((m1 - Mx) * kLog2e));
+    if (mrow0 + r < a.N) {
+      uint64_t* sp = a.stats + ((size_t)(rt * 256 + r) * a.nvt + vt) * 2;
+      put_tagged(sp, tag, Mx);
+      put_tagged(sp + 1, tag, S);
+    }
+  }
+
+  // rows r = vt, vt + nvt, ... of this row tile are merged here
+  uint32_t to = 0;
+  int nA = 0;
+  for (int r = vt; r < 256 && mrow0 + r < a.N; r += a.nvt) ++nA;
+  for (int p = tid; p < nA * a.nvt; p += 256) {
+    const int k = p / a.nvt, v2 = p % a.nvt, r = vt + k * a.nvt;
+    const int64_t y = ys[r];
+    if (y == a.ignore || y < 0 || y >= a.V) continue;
+    const uint64_t* sp = a.stats + ((size_t)(rt * 256 + r) * a.nvt + v2) * 2;
+    pm[p * 2] = get_tagged(sp, tag, to);
+    pm[p * 2 + 1] = get_tagged(sp + 1, tag, to);
+  }
+  __syncthreads();
+  if (tid < nA) {
+    const int r = vt + tid * a.nvt;
+    const int64_t R = mrow0 + r, y = ys[r];
+    float loss = 0.0f;
+    if (y != a.ignore) {
+      if (y < 0 || y >= a.V) {
+        loss = __builtin_nanf("");
+      } else {
+        float Mx = -INFINITY;
+        for (int v2 = 0; v2 < a.nvt; ++v2) Mx = fmaxf(Mx, pm[(tid * a.nvt + v2) * 2]);
+        float S = 0.0f;
+        for (int v2 = 0; v2 < a.nvt; ++v2) {
+          const float mv = pm[(tid * a.nvt + v2) * 2], sv = pm[(tid * a.nvt + v2) * 2 + 1];
+          if (mv != -INFINITY) S += sv * __builtin_amdgcn_exp2f((mv - Mx) * kLog2e);
+        }
+        const float xy = get_tagged(a.xy + R, tag, to);
+        const float ey = __builtin_amdgcn_exp2f((xy - Mx) * kLog2e);
+        const float St = S + ey;
+        const float l = Mx + logf(St), pcomp = S / St;
+        loss = (pcomp >= 0.5f) ? (l - xy) : log1pf(S / ey);
+        put_tagged(a.lse + R, tag, l);
+        put_tagged(a.pc + R, tag, pcomp);
+      }
+    }
+    a.loss_rows[R] = loss;
+  }
+  // every row of the tile: its lse and 1 - p_y
+  {
+    const int r = tid;
+    const int64_t R = mrow0 + r, y = ys[r];
+    float l = 0.0f, pcv = 0.0f;
+    if (R < a.N && y != a.ignore && y >= 0 && y < a.V) {
+      l = get_tagged(a.lse + R, tag, to);
+      pcv = get_tagged(a.pc + R, tag, to);
+    }
+    lrow[r] = l;
+    prow[r] = pcv;
+  }
+  if (to) atomicOr(sflag, 1u);
+  __syncthreads();
+  if (tid == 0 && sflag[0]) atomicOr(&a.hdr->status, kStatusSyncTimeout);
+  const bool bad_scale = sflag[0] != 0u;
+
+  // g from the accumulators: s 2^((x - lse) log2 e) off the label,
+  // -s (1 - p_y) on it, +0 on ignored rows and past the vocabulary, NaN on
+  // rows with a label outside [0, V)
+  const float lgs = (gs > 0.0f) ? log2f(gs) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = lg::acc_row(wm, i, v, lane);
+      const int64_t R = mrow0 + r;
+      if (R >= a.N) continue;
+      const int64_t y = ys[r];
+      const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
+      const float b = lrow[r] * kLog2e - lgs;
+      const float gy = -gs * prow[r];
+      uint16_t* grow = a.g + R * a.ldg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = n0 + lg::acc_col(wn, j, lane);
+        if (c >= a.ldg) continue;
+        float gv;
+        if (ign || c >= Nv) gv = 0.0f;
+        else if (bad || bad_scale) gv = __builtin_nanf("");
+        else if ((int64_t)c == y) gv = gy;
+        else if (gs > 0.0f) gv = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -b));
+        else gv = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -lrow[r] * kLog2e)) * gs;
+        grow[c] = to_bits<T>(gv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3-4. dh = g W and dW = g^T h (16-bit): MFMA tiles, 2^-k on output.
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const char* A;
+  int64_t lda;
+  const char* B;
+  int64_t ldb;
+  int M, N, K;
+  uint16_t* C;
+  int64_t ldc;
+  const LinHeader* hdr;
+};
+
+template <typename T, int AK, int BKD>
+__global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int mt = (a.M + 255) / 256, nt = (a.N + 255) / 256;
+  int mti, nti;
+  lg::tile_of(blockIdx.x, mt, nt, mti, nti);
+  const int m0 = mti * 256, n0 = nti * 256;
+  Tile t;
+  lg::tile_rs<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.M, a.N, a.K, m0, n0);
+  const float us = a.hdr->unscale;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = m0 + lg::acc_row(wm, i, v, lane);
+      if (r >= a.M) continue;
+      uint16_t* crow = a.C + (int64_t)r * a.ldc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = n0 + lg::acc_col(wn, j, lane);
+        if (c < a.N) crow[c] = to_bits<T>(t.acc[i][j][v] * us);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: a plain tiled GEMM (64 x 64 tiles, 4 x 4 outputs per lane,
+// fp32 FMA), element-wise loads of either operand layout:
+//   C[m][n] = alpha sum_k A(m, k) B(n, k) + beta C[m][n]
+//   A(m, k) = A[m lda + k] (AKO = 0) or A[k lda + m] (AKO = 1); B likewise.
+// ---------------------------------------------------------------------------
+template <bool AKO, bool BKO>
+__global__ __launch_bounds__(256) void lin_gemm_f32_kernel(const float* A, int64_t lda, const float* B, int64_t ldb,
+                                                           int M, int N, int K, float alpha, float beta, float* C,
+                                                           int64_t ldc) {
+  __shared__ float As[16][65], Bs[16][65];
+  const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = tid; e < 16 * 64; e += 256) {
+      const int kk = AKO ? e / 64 : e % 16, mm = AKO ? e % 64 : e / 16;
+      const int m = m0 + mm, k = k0 + kk;
+      As[kk][mm] = (m < M && k < K) ? (AKO ? A[(int64_t)k * lda + m] : A[(int64_t)m * lda + k]) : 0.0f;
+      const int kb = BKO ? e / 64 : e % 16, nn = BKO ? e % 64 : e / 16;
+      const int n = n0 + nn, kq = k0 + kb;
+      Bs[kb][nn] = (n < N && kq < K) ? (BKO ? B[(int64_t)kq * ldb + n] : B[(int64_t)n * ldb + kq]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_fmaf(As[kk][tm * 4 + x], Bs[kk][tn * 4 + y], acc[x][y]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int m = m0 + tm * 4 + x, n = n0 + tn * 4 + y;
+      if (m < M && n < N) {
+        float* c = C + (int64_t)m * ldc + n;
+        *c = alpha * acc[x][y] + (beta != 0.0f ? beta * *c : 0.0f);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shared small kernels.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lin_zero_kernel(uint16_t* dst, int64_t ld, int64_t cols, int esz) {
   if (esz == 4) {
     float* d = (float*)dst + (int64_t)blockIdx.x * ld;
@@ -204,53 +496,29 @@ __global__ __launch_bounds__(256) void lin_zero_kernel(uint16_t* dst, int64_t ld
   }
 }
 
-// dst[c][r] = src[r][c] for a rows x cols matrix of 16-bit elements (both
-// row-major, rows and cols multiples of 64): one 64 x 64 tile per workgroup,
-// read and written in 16-byte vectors, turned through LDS (rows padded to 66
-// elements so a column read falls in distinct banks).  It gives the
-// weight-gradient GEMM operands whose reduction dimension is contiguous.
-__global__ __launch_bounds__(256) void lin_transpose16_kernel(const uint16_t* src, int64_t ld_src, uint16_t* dst,
-                                                              int64_t ld_dst) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  __shared__ uint16_t tile[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int u = tid + h * 256, r = u >> 3, cv = (u & 7) * 8;
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(src + (r0 + r) * ld_src + c0 + cv));
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      tile[r][cv + 2 * d] = (uint16_t)(v[d] & 0xffffu);
-      tile[r][cv + 2 * d + 1] = (uint16_t)(v[d] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int u = tid + h * 256, c = u >> 3, rv = (u & 7) * 8;
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = (uint32_t)tile[rv + 2 * d][c] | ((uint32_t)tile[rv + 2 * d + 1][c] << 16);
-    __builtin_nontemporal_store(o, (u32x4*)(dst + (c0 + c) * ld_dst + r0 + rv));
-  }
-}
-
 // One workgroup: L = sum of the valid rows' losses / n, in row order (each
-// lane a contiguous slice, then a fixed tree), fp64; status = OR of the chunks'.
+// lane a contiguous slice, then a fixed tree), fp64; status from the labels
+// (a label outside [0, V)), the exchange's status word and the fp32 path's
+// per-chunk words.
 __global__ __launch_bounds__(kNT) void lin_finish_kernel(const float* loss_rows, const int64_t* labels, int64_t N,
-                                                         int64_t ignore, const int32_t* n_valid,
-                                                         const uint32_t* chunk_status, int nc, float* loss_mean,
-                                                         uint32_t* status) {
+                                                         int64_t V, int64_t ignore, const int32_t* n_valid,
+                                                         const uint32_t* chunk_status, int nc,
+                                                         const LinHeader* hdr, float* loss_mean, uint32_t* status) {
   __shared__ double acc[kNT];
   __shared__ uint32_t st[kNT];
   const int tid = threadIdx.x;
   const int64_t i0 = N * tid / kNT, i1 = N * (tid + 1) / kNT;
   double a = 0.0;
-  for (int64_t i = i0; i < i1; ++i)
-    if (labels[i] != ignore) a += (double)loss_rows[i];
   uint32_t s = 0;
-  for (int c = tid; c < nc; c += kNT) s |= chunk_status[c];
+  for (int64_t i = i0; i < i1; ++i) {
+    const int64_t y = labels[i];
+    if (y != ignore) {
+      a += (double)loss_rows[i];
+      if (y < 0 || y >= V) s |= kStatusLabelRange;
+    }
+  }
+  if (chunk_status)
+    for (int c = tid; c < nc; c += kNT) s |= chunk_status[c];
   acc[tid] = a;
   st[tid] = s;
   __syncthreads();
@@ -262,9 +530,14 @@ __global__ __launch_bounds__(kNT) void lin_finish_kernel(const float* loss_rows,
     __syncthreads();
   }
   if (tid == 0) {
-    loss_mean[0] = (float)(acc[0] / (double)n_valid[0]);
-    if (status) status[0] = st[0];
+    const uint32_t sw = st[0] | (hdr ? hdr->status : 0u);
+    loss_mean[0] = (sw & kStatusSyncTimeout) ? __builtin_nanf("") : (float)(acc[0] / (double)n_valid[0]);
+    if (status) status[0] = sw;
   }
+}
+
+__global__ __launch_bounds__(256) void lin_fill_kernel(uint32_t* p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_words; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
 
 __global__ void lin_empty_kernel(float* loss_mean, int32_t* n_valid, uint32_t* status) {
@@ -276,136 +549,203 @@ __global__ void lin_empty_kernel(float* loss_mean, int32_t* n_valid, uint32_t* s
 }
 
 // ---------------------------------------------------------------------------
-// rocBLAS: one handle per device for the process lifetime; calls on a device
-// are serialised around it (the handle's stream is set per call).
+// fp32 path layout: the chunk's fp32 logits (the gradient is written over
+// them), the cross-entropy workspace, per-chunk words.
 // ---------------------------------------------------------------------------
-constexpr int kMaxDevices = 64;
-std::mutex g_blas_mu[kMaxDevices];
-rocblas_handle g_blas[kMaxDevices];
-
-// hipBLASLt for the 16-bit GEMMs (its first heuristic choice measured 14-19%
-// faster than rocBLAS on the 4096 x 4096 x 32000 shapes); rocBLAS serves fp32
-// and any shape hipBLASLt offers no algorithm for.  Per device: one handle and
-// the descriptors and algorithm chosen for each GEMM shape, kept for the
-// process (host memory); no GEMM workspace is asked for.  Its scalars are
-// passed from the host: with device-resident scalars
-// (HIPBLASLT_POINTER_MODE_DEVICE) the installed hipBLASLt returned wrong
-// results (only element 0 of D right), so a GEMM whose alpha exists only on
-// the device (fp16's 2^-k) stays on rocBLAS.
-struct LtPlan {
-  bool ta, tb;
-  int64_t m, n, k, lda, ldb, ldc;
-  hipDataType ab, c;
-  bool ok;
-  hipblasLtMatmulDesc_t md;
-  hipblasLtMatrixLayout_t la, lb, lc;
-  hipblasLtMatmulAlgo_t algo;
+struct F32Layout {
+  size_t ce_ws, logits, dl_chunk, chunk_status, chunk_loss, chunk_n, total;
+  size_t ce_ws_bytes;
+  int64_t T;
+  int nc;
 };
-hipblasLtHandle_t g_lt[kMaxDevices];
-bool g_lt_failed[kMaxDevices];
-std::vector<LtPlan> g_plans[kMaxDevices];
-// Plans kept per device; past this many (callers whose row counts keep
-// changing) the oldest is destroyed, so the cache stays bounded.
-constexpr size_t kMaxPlans = 128;
-
-void destroy_plan(LtPlan& p) {
-  if (p.md) hipblasLtMatmulDescDestroy(p.md);
-  if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
-  if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
-  if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
-  p.md = nullptr;
-  p.la = p.lb = p.lc = nullptr;
+F32Layout f32_layout(int64_t N, int64_t V, int64_t chunk_rows) {
+  F32Layout L;
+  memset(&L, 0, sizeof(L));
+  int64_t t = chunk_rows > 0 ? chunk_rows : kF32ChunkRows;
+  const int64_t min_t = (N + kMaxChunks - 1) / kMaxChunks;
+  if (t < min_t) t = min_t;
+  L.T = (t + 63) / 64 * 64;
+  L.nc = (int)((N + L.T - 1) / L.T);
+  const int64_t Tc = (N < L.T) ? (N > 0 ? N : 1) : L.T;
+  L.ce_ws_bytes = ce_workspace_bytes(Tc, V, 0, CE_DTYPE_F32);
+  size_t off = sizeof(LinHeader);
+  L.ce_ws = align256(off);
+  off = L.ce_ws + align256(L.ce_ws_bytes);
+  L.logits = off;
+  off += align256((size_t)Tc * V * 4);
+  const size_t nc = (size_t)(L.nc > 0 ? L.nc : 1);
+  L.dl_chunk = off;
+  off += align256(nc * 4);
+  L.chunk_status = off;
+  off += align256(nc * 4);
+  L.chunk_loss = off;
+  off += align256(nc * 4);
+  L.chunk_n = off;
+  off += align256(nc * 4);
+  L.total = off;
+  return L;
 }
 
-// The plan for a GEMM shape (nullptr: hipBLASLt offers none).  Called with the
-// device's lock held; the pointer is valid until the next call.
-const LtPlan* lt_plan(int dev, bool ta, bool tb, int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
-                      int64_t ldc, hipDataType ab, hipDataType c) {
-  if (g_lt_failed[dev]) return nullptr;
-  if (g_lt[dev] == nullptr && hipblasLtCreate(&g_lt[dev]) != HIPBLAS_STATUS_SUCCESS) {
-    g_lt[dev] = nullptr;
-    g_lt_failed[dev] = true;
-    return nullptr;
+bool aligned16(const void* p, int64_t ld, int es) { return ((uintptr_t)p % 16 == 0) && ((ld * es) % 16 == 0); }
+
+template <typename K>
+int set_lds(K* fn, int bytes) {
+  return hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
+             ? CE_OK
+             : CE_ERR_HIP;
+}
+
+// The 16-bit path (T = __bf16 or _Float16).
+template <typename T>
+int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, const int64_t* labels, int64_t N,
+             int64_t H, int64_t V, int64_t ignore, const float* dloss, float* loss_mean, float* loss_rows,
+             int32_t* n_valid, uint32_t* status, void* gh, int64_t ldgh, void* gw, int64_t ldgw, char* ws,
+             const FastLayout& L, bool fp16, hipStream_t st) {
+  LinHeader* hdr = (LinHeader*)ws;
+  uint16_t* g = (uint16_t*)(ws + L.g);
+  hipLaunchKernelGGL(lin_prep_kernel, dim3(1), dim3(kNT), 0, st, labels, N, ignore, (int64_t)64, 1, dloss,
+                     fp16 ? 1 : 0, hdr, (float*)nullptr, n_valid);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  // fast operand loads need 16-byte rows and a hidden size of whole 16-byte chunks
+  const bool fast = aligned16(hidden, ldh, 2) && aligned16(weight, ldw, 2) && H % 8 == 0;
+  LogitsArgs la;
+  la.h = (const char*)hidden;
+  la.ldh = ldh;
+  la.w = (const char*)weight;
+  la.ldw = ldw;
+  la.labels = labels;
+  la.ignore = ignore;
+  la.N = N;
+  la.H = H;
+  la.V = V;
+  la.nvt = L.nvt;
+  la.hdr = hdr;
+  la.g = g;
+  la.ldg = L.ldg;
+  la.xy = (uint64_t*)(ws + L.xy);
+  la.lse = (uint64_t*)(ws + L.lse);
+  la.pc = (uint64_t*)(ws + L.pc);
+  la.loss_rows = loss_rows;
+  const int64_t rt_total = (N + 255) / 256;
+  auto kfn = fast ? lin_logits_ce_kernel<T, true, lg::kKC, lg::kKC> : lin_logits_ce_kernel<T, false, lg::kKCg, lg::kKCg>;
+  const int lds_bytes = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+  if (set_lds(kfn, lds_bytes) != CE_OK) return CE_ERR_HIP;
+  for (int c = 0; c < L.nchunks; ++c) {
+    const int64_t rt0 = (int64_t)c * L.rt_chunk;
+    const int rtc = (int)((rt_total - rt0 < L.rt_chunk) ? rt_total - rt0 : L.rt_chunk);
+    la.row0 = rt0 * 256;
+    la.rtc = rtc;
+    la.stats = (uint64_t*)(ws + L.stats) + (size_t)c * L.rt_chunk * 256 * L.nvt * 2;
+    void* params[] = {&la};
+    if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(rtc * L.nvt)), dim3(256), params, lds_bytes, st) !=
+        hipSuccess)
+      return CE_ERR_HIP;
   }
-  for (const LtPlan& p : g_plans[dev])
-    if (p.ta == ta && p.tb == tb && p.m == m && p.n == n && p.k == k && p.lda == lda && p.ldb == ldb &&
-        p.ldc == ldc && p.ab == ab && p.c == c)
-      return p.ok ? &p : nullptr;
-  LtPlan p;
-  memset(&p, 0, sizeof(p));
-  p.ta = ta, p.tb = tb, p.m = m, p.n = n, p.k = k, p.lda = lda, p.ldb = ldb, p.ldc = ldc, p.ab = ab, p.c = c;
-  const hipblasOperation_t oa = ta ? HIPBLAS_OP_T : HIPBLAS_OP_N, ob = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  uint64_t no_ws = 0;
-  hipblasLtMatmulHeuristicResult_t res;
-  int nres = 0;
-  p.ok = hipblasLtMatmulDescCreate(&p.md, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &oa, sizeof(oa)) ==
-             HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &ob, sizeof(ob)) ==
-             HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatrixLayoutCreate(&p.la, ab, ta ? k : m, ta ? m : k, lda) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatrixLayoutCreate(&p.lb, ab, tb ? n : k, tb ? k : n, ldb) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatrixLayoutCreate(&p.lc, c, m, n, ldc) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws,
-                                               sizeof(no_ws)) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulAlgoGetHeuristic(g_lt[dev], p.md, p.la, p.lb, p.lc, p.lc, pref, 1, &res, &nres) ==
-             HIPBLAS_STATUS_SUCCESS &&
-         nres > 0 && res.workspaceSize == 0;
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (p.ok) p.algo = res.algo;
-  else destroy_plan(p);  // remembered as unavailable: rocBLAS serves the shape
-  if (g_plans[dev].size() >= kMaxPlans) {
-    destroy_plan(g_plans[dev].front());
-    g_plans[dev].erase(g_plans[dev].begin());
+  if (gh) {  // dh [N, H] = g [N, V] W [V, H]
+    BwdArgs b;
+    b.A = (const char*)g;
+    b.lda = L.ldg;
+    b.B = (const char*)weight;
+    b.ldb = ldw;
+    b.M = (int)N;
+    b.N = (int)H;
+    b.K = (int)V;
+    b.C = (uint16_t*)gh;
+    b.ldc = ldgh;
+    b.hdr = hdr;
+    auto fn = fast ? lin_bwd_kernel<T, lg::kKC, lg::kKO> : lin_bwd_kernel<T, lg::kKC, lg::kKOg>;
+    if (set_lds(fn, 2 * lg::kStageBytes) != CE_OK) return CE_ERR_HIP;
+    const int64_t grid = ((N + 255) / 256) * ((H + 255) / 256);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 2 * lg::kStageBytes, st, b);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
-  g_plans[dev].push_back(p);
-  return p.ok ? &g_plans[dev].back() : nullptr;
+  if (gw) {  // dW [V, H] = g^T h: A(v, tok) = g[tok][v], B(h, tok) = h[tok][h]
+    BwdArgs b;
+    b.A = (const char*)g;
+    b.lda = L.ldg;
+    b.B = (const char*)hidden;
+    b.ldb = ldh;
+    b.M = (int)V;
+    b.N = (int)H;
+    b.K = (int)N;
+    b.C = (uint16_t*)gw;
+    b.ldc = ldgw;
+    b.hdr = hdr;
+    auto fn = fast ? lin_bwd_kernel<T, lg::kKO, lg::kKO> : lin_bwd_kernel<T, lg::kKO, lg::kKOg>;
+    if (set_lds(fn, 2 * lg::kStageBytes) != CE_OK) return CE_ERR_HIP;
+    const int64_t grid = ((V + 255) / 256) * ((H + 255) / 256);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 2 * lg::kStageBytes, st, b);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  }
+  hipLaunchKernelGGL(lin_finish_kernel, dim3(1), dim3(kNT), 0, st, loss_rows, labels, N, V, ignore, n_valid,
+                     (const uint32_t*)nullptr, 0, (const LinHeader*)hdr, loss_mean, status);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
-rocblas_datatype blas_type(int dtype) {
-  if (dtype == CE_DTYPE_BF16) return rocblas_datatype_bf16_r;
-  if (dtype == CE_DTYPE_F16) return rocblas_datatype_f16_r;
-  return rocblas_datatype_f32_r;
+int launch_f32_gemm(bool ako, bool bko, const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N, int K,
+                    float alpha, float beta, float* C, int64_t ldc, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+  if (!ako && !bko) hipLaunchKernelGGL((lin_gemm_f32_kernel<false, false>), grid, dim3(256), 0, st, A, lda, B, ldb, M, N, K, alpha, beta, C, ldc);
+  else if (!ako && bko) hipLaunchKernelGGL((lin_gemm_f32_kernel<false, true>), grid, dim3(256), 0, st, A, lda, B, ldb, M, N, K, alpha, beta, C, ldc);
+  else if (ako && !bko) hipLaunchKernelGGL((lin_gemm_f32_kernel<true, false>), grid, dim3(256), 0, st, A, lda, B, ldb, M, N, K, alpha, beta, C, ldc);
+  else hipLaunchKernelGGL((lin_gemm_f32_kernel<true, true>), grid, dim3(256), 0, st, A, lda, B, ldb, M, N, K, alpha, beta, C, ldc);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
-hipDataType lt_type(rocblas_datatype t) {
-  return t == rocblas_datatype_bf16_r ? HIP_R_16BF : (t == rocblas_datatype_f16_r ? HIP_R_16F : HIP_R_32F);
-}
-
-// A GEMM scalar: its device copy, and its value when the host knows it (NaN
-// when only the device does).
-struct Scalar {
-  const float* dev;
-  float host;
-};
-
-// D = alpha op(A) op(B) + beta C (column-major, as BLAS): hipBLASLt for
-// 16-bit inputs when both scalars are known on the host and it has an
-// algorithm for the shape, else rocBLAS with the device scalars.
-int gemm(int dev, rocblas_handle h, hipStream_t st, rocblas_operation ta, rocblas_operation tb, int64_t m, int64_t n,
-         int64_t k, Scalar alpha_s, const void* A, rocblas_datatype at, int64_t lda, const void* B,
-         rocblas_datatype bt, int64_t ldb, Scalar beta_s, void* C, rocblas_datatype ct, int64_t ldc) {
-  if (at != rocblas_datatype_f32_r && !isnan(alpha_s.host) && !isnan(beta_s.host)) {
-    const LtPlan* p = lt_plan(dev, ta == rocblas_operation_transpose, tb == rocblas_operation_transpose, m, n, k, lda,
-                              ldb, ldc, lt_type(at), lt_type(ct));
-    if (p) {
-      const hipblasStatus_t s = hipblasLtMatmul(g_lt[dev], p->md, &alpha_s.host, A, p->la, B, p->lb, &beta_s.host, C,
-                                                p->lc, C, p->lc, &p->algo, nullptr, 0, st);
-      return s == HIPBLAS_STATUS_SUCCESS ? CE_OK : CE_ERR_HIP;
+// The fp32 path, chunk by chunk.
+int run_f32(const float* h, int64_t ldh, const float* w, int64_t ldw, const int64_t* labels, int64_t N, int64_t H,
+            int64_t V, int64_t ignore, const float* dloss, float* loss_mean, float* loss_rows, int32_t* n_valid,
+            uint32_t* status, float* gh, int64_t ldgh, float* gw, int64_t ldgw, char* ws, const F32Layout& L,
+            hipStream_t st) {
+  float* logits = (float*)(ws + L.logits);
+  float* dl_chunk = (float*)(ws + L.dl_chunk);
+  uint32_t* chunk_status = (uint32_t*)(ws + L.chunk_status);
+  float* chunk_loss = (float*)(ws + L.chunk_loss);
+  int32_t* chunk_n = (int32_t*)(ws + L.chunk_n);
+  // the chunks' cross-entropy workspace starts from zero in every call (the
+  // same workspace may have served the 16-bit layout in between)
+  const size_t words = L.ce_ws_bytes / 4;
+  hipLaunchKernelGGL(lin_fill_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                     dim3(256), 0, st, (uint32_t*)(ws + L.ce_ws), words);
+  hipLaunchKernelGGL(lin_prep_kernel, dim3(1), dim3(kNT), 0, st, labels, N, ignore, L.T, L.nc, dloss, 0,
+                     (LinHeader*)nullptr, dl_chunk, n_valid);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  for (int c = 0; c < L.nc; ++c) {
+    const int64_t r0 = (int64_t)c * L.T;
+    const int64_t Tc = (N - r0 < L.T) ? N - r0 : L.T;
+    const float* hc = h + r0 * ldh;
+    int rc = launch_f32_gemm(false, false, hc, ldh, w, ldw, (int)Tc, (int)V, (int)H, 1.0f, 0.0f, logits, V, st);
+    if (rc != CE_OK) return rc;
+    // the chunk's dloss share dloss n_c / n: its scale dloss' / n_c is the batch's
+    rc = ce_fwd_bwd_inplace(logits, V, labels + r0, Tc, V, CE_DTYPE_F32, ignore, 0, dl_chunk + c, chunk_loss + c,
+                            loss_rows + r0, nullptr, nullptr, chunk_n + c, chunk_status + c, ws + L.ce_ws,
+                            L.ce_ws_bytes, st);
+    if (rc != CE_OK) return rc;
+    if (gh) {  // dh_c = g_c W: B(n = h, k = v) = W[v][h]
+      rc = launch_f32_gemm(false, true, logits, V, w, ldw, (int)Tc, (int)H, (int)V, 1.0f, 0.0f, gh + r0 * ldgh, ldgh,
+                           st);
+      if (rc != CE_OK) return rc;
+    }
+    if (gw) {  // dW += g_c^T h_c: A(m = v, k = tok) = g[tok][v], B(n = h, k = tok) = h[tok][h]
+      rc = launch_f32_gemm(true, true, logits, V, hc, ldh, (int)V, (int)H, (int)Tc, 1.0f, c == 0 ? 0.0f : 1.0f, gw,
+                           ldgw, st);
+      if (rc != CE_OK) return rc;
     }
   }
-  const float* alpha = alpha_s.dev;
-  const float* beta = beta_s.dev;
-  const rocblas_status s =
-      rocblas_gemm_ex(h, ta, tb, (rocblas_int)m, (rocblas_int)n, (rocblas_int)k, alpha, A, at, (rocblas_int)lda, B, bt,
-                      (rocblas_int)ldb, beta, C, ct, (rocblas_int)ldc, C, ct, (rocblas_int)ldc,
-                      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return s == rocblas_status_success ? CE_OK : CE_ERR_HIP;
+  hipLaunchKernelGGL(lin_finish_kernel, dim3(1), dim3(kNT), 0, st, loss_rows, labels, N, V, ignore, n_valid,
+                     (const uint32_t*)chunk_status, L.nc, (const LinHeader*)nullptr, loss_mean, status);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
-bool fits32(int64_t x) { return x >= 0 && x < ((int64_t)1 << 31); }
+size_t workspace_for(int64_t N, int64_t H, int64_t V, int64_t chunk_rows, int dtype) {
+  (void)H;
+  if (dtype == CE_DTYPE_F32) {
+    const F32Layout L = f32_layout(N, V, chunk_rows);
+    return L.ce_ws_bytes ? L.total : 0;
+  }
+  const int64_t cus = device_cus();
+  return fast_layout(N, V, cus > 0 ? cus : 256).total;
+}
 
 }  // namespace
 
@@ -415,9 +755,7 @@ size_t ce_linear_workspace_bytes(int64_t n_rows, int64_t hidden_size, int64_t vo
                                  int dtype) {
   if (!valid_dtype(dtype) || n_rows < 0 || hidden_size < 1 || vocab < 1 || chunk_rows < 0) return 0;
   if (!fits32(n_rows) || !fits32(hidden_size) || !fits32(vocab)) return 0;
-  const LinLayout L = lin_layout(n_rows, hidden_size, vocab, chunk_rows, dtype);
-  if (L.ce_ws_bytes == 0) return 0;
-  return L.total;
+  return workspace_for(n_rows, hidden_size, vocab, chunk_rows, dtype);
 }
 
 int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight, int64_t ld_weight,
@@ -443,12 +781,16 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
   if (!fits32(N) || !fits32(H) || !fits32(V) || !fits32(ld_hidden) || !fits32(ld_weight) ||
       !fits32(ld_grad_hidden) || !fits32(ld_grad_weight))
     return CE_ERR_UNSUPPORTED;
-  const LinLayout L = lin_layout(N, H, V, chunk_rows, dtype);
-  if (L.ce_ws_bytes == 0) return CE_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < L.total || (uintptr_t)workspace % 256) return CE_ERR_WORKSPACE;
+  // buffer resources address each operand with 32-bit offsets below 2^31
+  const int64_t lim = (int64_t)1 << 31;
+  if ((N + 256) * ld_hidden * es >= lim || (V + 256) * ld_weight * es >= lim ||
+      (N + 256) * ((V + 7) / 8 * 8) * es >= lim)
+    return CE_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(N, H, V, chunk_rows, dtype);
+  if (need == 0) return CE_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < need || (uintptr_t)workspace % 256) return CE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-
   if (N == 0) {
     hipLaunchKernelGGL(lin_empty_kernel, dim3(1), dim3(64), 0, st, loss_mean, n_valid, status);
     if (grad_weight)
@@ -456,133 +798,20 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
                          ld_grad_weight, H, es);
     return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
   }
-
-  float* logits = (float*)(ws + L.logits);
-  float* dl_chunk = (float*)(ws + L.dl_chunk);
-  uint32_t* chunk_status = (uint32_t*)(ws + L.chunk_status);
-  float* chunk_loss = (float*)(ws + L.chunk_loss);
-  int32_t* chunk_n = (int32_t*)(ws + L.chunk_n);
-  void* g_lo = (dtype == CE_DTYPE_F32) ? (void*)logits : (void*)(ws + L.g16);
-  // the weight gradient: accumulated over chunks in fp32 (the output itself for
-  // fp32, else a workspace copy rounded once at the end); a single chunk is
-  // written by its GEMM in the output format (fp32 accumulation, one rounding)
-  const bool dw_direct = dtype == CE_DTYPE_F32 || L.nc == 1;
-  float* dw32 = dw_direct ? (float*)grad_weight : (float*)(ws + L.dw32);
-  const int64_t ld_dw = dw_direct ? ld_grad_weight : H;
-  const rocblas_datatype dt = blas_type(dtype);
-  const float* cs = (const float*)(ws + L.consts);  // 1, 0, 2^-k on the device
-  const Scalar one = {cs, 1.0f}, zero = {cs + 1, 0.0f};
-  const Scalar down = {cs + 2, dtype == CE_DTYPE_F16 ? NAN : 1.0f};  // 2^-k: k = 0 unless fp16
-
-  hipLaunchKernelGGL(lin_prep_kernel, dim3(1), dim3(kNT), 0, st, labels, N, ignore_index, L.T, L.nc, dloss,
-                     dtype == CE_DTYPE_F16 ? 1 : 0, dl_chunk, n_valid, (float*)(ws + L.consts));
-  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
-
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CE_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_blas_mu[dev]);
-  if (g_blas[dev] == nullptr) {
-    if (rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-      g_blas[dev] = nullptr;
-      return CE_ERR_HIP;
-    }
-    // GEMM kernels that accumulate with atomics would make results depend on
-    // timing: the call is deterministic like the rest of the library
-    rocblas_set_atomics_mode(g_blas[dev], rocblas_atomics_not_allowed);
-  }
-  rocblas_handle bh = g_blas[dev];
-  if (rocblas_set_stream(bh, st) != rocblas_status_success ||
-      rocblas_set_pointer_mode(bh, rocblas_pointer_mode_device) != rocblas_status_success)
-    return CE_ERR_HIP;
-
-  const char* hb = (const char*)hidden;
-  int rc = CE_OK;
-  for (int c = 0; c < L.nc && rc == CE_OK; ++c) {
-    const int64_t r0 = (int64_t)c * L.T;
-    const int64_t Tc = (N - r0 < L.T) ? N - r0 : L.T;
-    const void* hc = hb + r0 * ld_hidden * es;
-    // 1. logits_c [Tc x V] = h_c W^T  (column-major: V x Tc = (H x V)^T (H x Tc))
-    rc = gemm(dev, bh, st, rocblas_operation_transpose, rocblas_operation_none, V, Tc, H, one, weight, dt, ld_weight,
-              hc, dt, ld_hidden, zero, logits, rocblas_datatype_f32_r, V);
-    if (rc != CE_OK) break;
-    // 2-3. the chunk's losses and g: for bf16 / fp16 one kernel reads the fp32
-    // logits and writes g in the input format for the GEMMs; otherwise (fp32,
-    // or rows it does not serve) g is written over the fp32 logits and cast
-    bool fused = false;
-    if (dtype != CE_DTYPE_F32) {
-      rc = ce_lin_chunk_f32_to16(logits, V, labels + r0, Tc, V, dtype, ignore_index, dl_chunk + c, chunk_loss + c,
-                                 loss_rows + r0, chunk_n + c, chunk_status + c, g_lo, V, ws + L.ce_ws,
-                                 L.ce_ws_bytes, st);
-      if (rc == CE_OK) fused = true;
-      else if (rc != CE_ERR_UNSUPPORTED) break;
-    }
-    if (!fused) {
-      rc = ce_fwd_bwd_inplace(logits, V, labels + r0, Tc, V, CE_DTYPE_F32, ignore_index, 0, dl_chunk + c,
-                              chunk_loss + c, loss_rows + r0, nullptr, nullptr, chunk_n + c, chunk_status + c,
-                              ws + L.ce_ws, L.ce_ws_bytes, st);
-      if (rc != CE_OK) break;
-      if (dtype == CE_DTYPE_BF16)
-        hipLaunchKernelGGL(lin_cast_kernel<__bf16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
-                           (__bf16*)g_lo, V, (const float*)nullptr);
-      else if (dtype == CE_DTYPE_F16)
-        hipLaunchKernelGGL(lin_cast_kernel<_Float16>, dim3((unsigned)Tc), dim3(256), 0, st, logits, V, V,
-                           (_Float16*)g_lo, V, (const float*)nullptr);
-      if (hipGetLastError() != hipSuccess) {
-        rc = CE_ERR_HIP;
-        break;
-      }
-    }
-    if (grad_hidden == nullptr && grad_weight == nullptr) continue;
-    // 4. dh_c [Tc x H] = g W  (column-major: H x Tc = (H x V)(V x Tc))
-    if (grad_hidden) {
-      rc = gemm(dev, bh, st, rocblas_operation_none, rocblas_operation_none, H, Tc, V, down, weight, dt, ld_weight,
-                g_lo, dt, V, zero, (char*)grad_hidden + r0 * ld_grad_hidden * es, dt, ld_grad_hidden);
-      if (rc != CE_OK) break;
-    }
-    // 5. dW [V x H] += g^T h_c  (column-major: H x V = (H x Tc)(Tc x V)): NT on
-    // the stored operands, or TN on transposed copies gT [V x Tc], hT [H x Tc]
-    if (grad_weight) {
-      rocblas_operation oa = rocblas_operation_none, ob = rocblas_operation_transpose;
-      const void *A = hc, *B = g_lo;
-      int64_t lda = ld_hidden, ldb = V;
-      if (L.tn && (uintptr_t)hc % 16 == 0 && ld_hidden % 8 == 0) {
-        uint16_t* gT = (uint16_t*)(ws + L.gT);
-        uint16_t* hT = (uint16_t*)(ws + L.hT);
-        hipLaunchKernelGGL(lin_transpose16_kernel, dim3((unsigned)(V / 64), (unsigned)(Tc / 64)), dim3(256), 0, st,
-                           (const uint16_t*)g_lo, V, gT, Tc);
-        hipLaunchKernelGGL(lin_transpose16_kernel, dim3((unsigned)(H / 64), (unsigned)(Tc / 64)), dim3(256), 0, st,
-                           (const uint16_t*)hc, ld_hidden, hT, Tc);
-        if (hipGetLastError() != hipSuccess) {
-          rc = CE_ERR_HIP;
-          break;
-        }
-        oa = rocblas_operation_transpose;
-        ob = rocblas_operation_none;
-        A = hT;
-        B = gT;
-        lda = ldb = Tc;
-      }
-      if (dw_direct)  // fp32: accumulate in the output; one 16-bit chunk: scale by 2^-k and round once
-        rc = gemm(dev, bh, st, oa, ob, H, V, Tc, dtype == CE_DTYPE_F32 ? one : down, A, dt, lda, B, dt, ldb,
-                  c == 0 ? zero : one, dw32, dtype == CE_DTYPE_F32 ? rocblas_datatype_f32_r : dt, ld_dw);
-      else
-        rc = gemm(dev, bh, st, oa, ob, H, V, Tc, one, A, dt, lda, B, dt, ldb, c == 0 ? zero : one, dw32,
-                  rocblas_datatype_f32_r, ld_dw);
-      if (rc != CE_OK) break;
-    }
-  }
-  if (rc != CE_OK) return rc;
-  if (grad_weight && !dw_direct) {
-    if (dtype == CE_DTYPE_BF16)
-      hipLaunchKernelGGL(lin_cast_kernel<__bf16>, dim3((unsigned)V), dim3(256), 0, st, dw32, H, H,
-                         (__bf16*)grad_weight, ld_grad_weight, down.dev);
-    else
-      hipLaunchKernelGGL(lin_cast_kernel<_Float16>, dim3((unsigned)V), dim3(256), 0, st, dw32, H, H,
-                         (_Float16*)grad_weight, ld_grad_weight, down.dev);
-  }
-  hipLaunchKernelGGL(lin_finish_kernel, dim3(1), dim3(kNT), 0, st, loss_rows, labels, N, ignore_index, n_valid,
-                     chunk_status, L.nc, loss_mean, status);
-  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+  if (dtype == CE_DTYPE_F32)
+    return run_f32((const float*)hidden, ld_hidden, (const float*)weight, ld_weight, labels, N, H, V, ignore_index,
+                   dloss, loss_mean, loss_rows, n_valid, status, (float*)grad_hidden, ld_grad_hidden,
+                   (float*)grad_weight, ld_grad_weight, ws, f32_layout(N, V, chunk_rows), st);
+  const int64_t cus = device_cus();
+  const FastLayout L = fast_layout(N, V, cus > 0 ? cus : 256);
+  if (L.nvt > (cus > 0 ? cus : 256)) return CE_ERR_UNSUPPORTED;  // a row tile's vocabulary tiles must be co-resident
+  if (dtype == CE_DTYPE_BF16)
+    return run_fast<__bf16>(hidden, ld_hidden, weight, ld_weight, labels, N, H, V, ignore_index, dloss, loss_mean,
+                            loss_rows, n_valid, status, grad_hidden, ld_grad_hidden, grad_weight, ld_grad_weight, ws,
+                            L, false, st);
+  return run_fast<_Float16>(hidden, ld_hidden, weight, ld_weight, labels, N, H, V, ignore_index, dloss, loss_mean,
+                            loss_rows, n_valid, status, grad_hidden, ld_grad_hidden, grad_weight, ld_grad_weight, ws,
+                            L, true, st);
 }
 
 }  // extern "C"

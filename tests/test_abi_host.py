@@ -165,11 +165,13 @@ def linear(lib, hidden=FAKE, ldh=64, weight=FAKE, ldw=64, labels=FAKE, N=8, H=64
 
 def test_linear_workspace_bytes(lib):
     b = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_BF16)
-    # one fp32 chunk of logits, its bf16 gradient and the fp32 weight-gradient accumulator
-    assert b >= 1024 * 32000 * 4 + 1024 * 32000 * 2 + 32000 * 4096 * 4
+    # 16-bit: the batch's gradient g in the input format and the small tagged
+    # exchange arrays -- no fp32 logits, no transposed copies
+    assert 4096 * 32000 * 2 <= b < 4096 * 32000 * 2 + (64 << 20)
+    assert lib.ce_linear_workspace_bytes(4096, 4096, 32000, 64, 1) == b  # chunk_rows does not enter
     f32 = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_F32)
-    assert 1024 * 32000 * 4 <= f32 < b  # fp32: no rounded copy, accumulates in the output
-    assert lib.ce_linear_workspace_bytes(4096, 4096, 32000, 64, 1) < b  # smaller chunks, smaller workspace
+    assert 1024 * 32000 * 4 <= f32 < 1024 * 32000 * 4 + (64 << 20)  # one fp32 chunk of logits
+    assert lib.ce_linear_workspace_bytes(4096, 4096, 32000, 64, _lib.CE_DTYPE_F32) < f32  # smaller chunks
     assert lib.ce_linear_workspace_bytes(-1, 64, 10, 0, 1) == 0
     assert lib.ce_linear_workspace_bytes(4, 0, 10, 0, 1) == 0
     assert lib.ce_linear_workspace_bytes(4, 64, 10, -1, 1) == 0
