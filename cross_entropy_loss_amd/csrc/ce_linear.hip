@@ -239,6 +239,13 @@ struct LogitsArgs {
   float* loss_rows;
 };
 
+// LDS: the K loop's stages (128 KB or 64 KB), then the epilogue's statistics
+// (16 KB + a 72 KB transpose area) and four staged 128 x 136 gradient
+// quarters (136 KB) at offset 16 KB: all of a CU's 160 KB.
+constexpr int kLogitsLds = 160 * 1024;
+static_assert(16384 + 4 * 128 * 136 * 2 <= kLogitsLds, "staged gradient quarters");
+static_assert(16384 + 256 * 72 * 4 <= kLogitsLds, "statistics transpose");
+
 template <typename T, bool DMA, int AK, int BKD>
 __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -254,60 +261,103 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   const float gs = a.hdr->gscale;
   __syncthreads();  // every wave is done with the K loop's LDS
 
+  // LDS after the K loop: per-row label data and statistics, and a
+  // [256][kPS] transpose area for the per-lane partials (kPS = 72 floats per
+  // row puts the two half-waves, four rows apart, on disjoint banks).  The
+  // epilogue walks the accumulators one 32-row block (index i) at a time so
+  // that only that block's row constants are held in registers.
+  constexpr int kPS = 72;
   int64_t* ys = (int64_t*)lds;              // [256] labels of the tile's rows
-  float* red = (float*)(lds + 2048);         // [2 waves][256 rows][2]
+  int32_t* yrel = (int32_t*)(lds + 2048);   // [256] label column - n0 when in this tile, else -1
+  float* mrow = (float*)(lds + 3072);       // [256] the tile's row max
+  float* xyl = (float*)(lds + 4096);        // [256 + 64] label logits found here (+ junk slots)
   float* pm = (float*)(lds + 6144);         // merge inputs: [<= 512][2]
   float* lrow = (float*)(lds + 10240);      // [256] lse of the tile's rows
   float* prow = (float*)(lds + 11264);      // [256] 1 - p_y
   uint32_t* sflag = (uint32_t*)(lds + 12288);
+  float* part = (float*)(lds + 16384);      // [256][kPS]
   if (tid == 0) sflag[0] = 0u;
   {
     const int64_t R = mrow0 + tid;
-    ys[tid] = (R < a.N) ? a.labels[R] : a.ignore;
+    const int64_t y = (R < a.N) ? a.labels[R] : a.ignore;
+    ys[tid] = y;
+    yrel[tid] = (y != a.ignore && y >= n0 && y < n0 + 256 && y < a.V) ? (int)(y - n0) : -1;
   }
   __syncthreads();
-
-  // the tile's per-row (max, label-excluded sum), this wave's 128 columns
+  const int lc = wn * 128 + (lane & 31);  // this lane's column in block j: lc + 32 j
+  bool cvalid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cvalid[j] = n0 + lc + 32 * j < Nv;
+  // pass A: per lane and row the max over its four columns, through LDS to
+  // one thread per row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float m[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m[v] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x16 blk = t.acc[i][j];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m[v] = fmaxf(m[v], cvalid[j] ? blk[v] : -INFINITY);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[lg::acc_row(wm, i, v, lane) * kPS + wn * 32 + (lane & 31)] = m[v];
+  }
+  __syncthreads();
+  {
+    const float* pr = part + tid * kPS;
+    float m = pr[0];
+#pragma unroll 8
+    for (int q = 1; q < 64; ++q) m = fmaxf(m, pr[q]);
+    mrow[tid] = m;
+  }
+  __syncthreads();
+  // pass B: the label-excluded sums relative to the row max; the lane that
+  // holds a row's label logit leaves it in xyl (others write a junk slot)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float mc[16], sv[16], xv[16];
+    int lj[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = lg::acc_row(wm, i, v, lane);
-      const int64_t y = ys[r];
-      float m = -INFINITY;
+      const float mr = mrow[r];
+      mc[v] = (mr == -INFINITY) ? 0.0f : mr * kLog2e;
+      const int d = yrel[r] - lc;  // the label's column is this lane's in block d / 32
+      lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
+      sv[v] = 0.0f;
+      xv[v] = 0.0f;
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = n0 + lg::acc_col(wn, j, lane);
-        if (c < Nv) m = fmaxf(m, t.acc[i][j][v]);
-      }
-      m = half_max(m);
-      float s = 0.0f;
-      const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
+    for (int j = 0; j < 4; ++j) {
+      const f32x16 blk = t.acc[i][j];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = n0 + lg::acc_col(wn, j, lane);
-        const float x = t.acc[i][j][v];
-        if (c < Nv && (int64_t)c != y) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mc));
-        if ((int64_t)c == y && mrow0 + r < a.N) put_tagged(a.xy + mrow0 + r, tag, x);
+      for (int v = 0; v < 16; ++v) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
+        sv[v] += (cvalid[j] && lj[v] != j) ? e : 0.0f;
+        xv[v] = (lj[v] == j) ? blk[v] : xv[v];
       }
-      s = half_sum(s);
-      if ((lane & 31) == 0) {
-        red[(wn * 256 + r) * 2] = m;
-        red[(wn * 256 + r) * 2 + 1] = s;
-      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = lg::acc_row(wm, i, v, lane);
+      part[r * kPS + wn * 32 + (lane & 31)] = sv[v];
+      xyl[(lj[v] >= 0) ? r : 256 + lane] = xv[v];
     }
   }
   __syncthreads();
   {
     const int r = tid;
-    const float m0 = red[r * 2], s0 = red[r * 2 + 1], m1 = red[(256 + r) * 2], s1 = red[(256 + r) * 2 + 1];
-    const float Mx = fmaxf(m0, m1);
-    const float S = ((m0 == -INFINITY) ? 0.0f : s0 * __builtin_amdgcn_exp2f((m0 - Mx) * kLog2e)) +
-                    ((m1 == -INFINITY) ? 0.0f : s1 * __builtin_amdgcn_exp2f((m1 - Mx) * kLog2e));
+    const float* pr = part + r * kPS;
+    float S = 0.0f;
+#pragma unroll 8
+    for (int q = 0; q < 64; ++q) S += pr[q];
     if (mrow0 + r < a.N) {
       uint64_t* sp = a.stats + ((size_t)(rt * 256 + r) * a.nvt + vt) * 2;
-      put_tagged(sp, tag, Mx);
+      put_tagged(sp, tag, mrow[r]);
       put_tagged(sp + 1, tag, S);
+      if (yrel[r] >= 0) put_tagged(a.xy + mrow0 + r, tag, xyl[r]);
     }
   }
 
@@ -369,32 +419,54 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
 
   // g from the accumulators: s 2^((x - lse) log2 e) off the label,
   // -s (1 - p_y) on it, +0 on ignored rows and past the vocabulary, NaN on
-  // rows with a label outside [0, V)
+  // rows with a label outside [0, V).  Each wave stages its 128 x 128
+  // quarter in LDS (rows of 272 bytes) and writes it out as 16-byte vectors.
   const float lgs = (gs > 0.0f) ? log2f(gs) : 0.0f;
+  constexpr int kGS = 136;  // staged row stride in elements
+  __syncthreads();  // the statistics area is free
+  uint16_t* stg = (uint16_t*)(lds + 16384 + wave * (128 * kGS * 2));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float bv[16], gyv[16], mul[16];
+    int lj[16], kind[16];  // kind: 0 normal, 1 zero (ignored row), 2 NaN (bad label or failed exchange)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = lg::acc_row(wm, i, v, lane);
-      const int64_t R = mrow0 + r;
-      if (R >= a.N) continue;
       const int64_t y = ys[r];
       const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
-      const float b = lrow[r] * kLog2e - lgs;
-      const float gy = -gs * prow[r];
-      uint16_t* grow = a.g + R * a.ldg;
+      kind[v] = ign ? 1 : ((bad || bad_scale) ? 2 : 0);
+      // g = 2^(x log2 e - b) * mul: b folds log2 s in when s > 0
+      bv[v] = lrow[r] * kLog2e - (gs > 0.0f ? lgs : 0.0f);
+      mul[v] = (gs > 0.0f) ? 1.0f : gs;
+      gyv[v] = -gs * prow[r];
+      const int d = yrel[r] - lc;
+      lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = n0 + lg::acc_col(wn, j, lane);
-        if (c >= a.ldg) continue;
-        float gv;
-        if (ign || c >= Nv) gv = 0.0f;
-        else if (bad || bad_scale) gv = __builtin_nanf("");
-        else if ((int64_t)c == y) gv = gy;
-        else if (gs > 0.0f) gv = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -b));
-        else gv = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -lrow[r] * kLog2e)) * gs;
-        grow[c] = to_bits<T>(gv);
+    for (int j = 0; j < 4; ++j) {
+      const f32x16 blk = t.acc[i][j];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float gv = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])) * mul[v];
+        gv = (lj[v] == j) ? gyv[v] : gv;
+        gv = (kind[v] == 2) ? __builtin_nanf("") : gv;
+        gv = (kind[v] == 1 || !cvalid[j]) ? 0.0f : gv;
+        const int r = lg::acc_row(wm, i, v, lane);
+        stg[(r - wm * 128) * kGS + (lc - wn * 128) + 32 * j] = to_bits<T>(gv);
       }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+  // 128 rows x 16 vectors of the quarter: four rows per pass of the wave
+  const int64_t cbase = (int64_t)n0 + wn * 128;
+#pragma unroll 4
+  for (int q = 0; q < 32; ++q) {
+    const int rr = q * 4 + (lane >> 4), cv = (lane & 15) * 8;
+    const int64_t R = mrow0 + wm * 128 + rr;
+    const int64_t c = cbase + cv;
+    if (R < a.N && c < a.ldg) {
+      const lg::u32x4 val = *(const lg::u32x4*)(stg + rr * kGS + cv);
+      *(lg::u32x4*)(a.g + R * a.ldg + c) = val;
     }
   }
 }
@@ -628,7 +700,7 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
   la.loss_rows = loss_rows;
   const int64_t rt_total = (N + 255) / 256;
   auto kfn = fast ? lin_logits_ce_kernel<T, true, lg::kKC, lg::kKC> : lin_logits_ce_kernel<T, false, lg::kKCg, lg::kKCg>;
-  const int lds_bytes = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+  const int lds_bytes = kLogitsLds;
   if (set_lds(kfn, lds_bytes) != CE_OK) return CE_ERR_HIP;
   for (int c = 0; c < L.nchunks; ++c) {
     const int64_t rt0 = (int64_t)c * L.rt_chunk;
