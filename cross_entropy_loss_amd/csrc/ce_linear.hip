@@ -480,12 +480,16 @@ struct BwdArgs {
   const char* B;
   int64_t ldb;
   int M, N, K;
+  int Mx, Nx;  // loadable extents along M / N (at least M / N)
   uint16_t* C;
   int64_t ldc;
   const LinHeader* hdr;
 };
 
-template <typename T, int AK, int BKD>
+// DMA: both operands through direct-to-LDS loads (16-byte aligned rows;
+// a.Mx / a.Nx bound the 16-byte chunks a KO operand may load), kLdsBytes of
+// LDS; otherwise the register-staged loop, 2 kStageBytes.
+template <typename T, int AK, int BKD, bool DMA>
 __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int mt = (a.M + 255) / 256, nt = (a.N + 255) / 256;
@@ -493,7 +497,8 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
   lg::tile_of(blockIdx.x, mt, nt, mti, nti);
   const int m0 = mti * 256, n0 = nti * 256;
   Tile t;
-  lg::tile_rs<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.M, a.N, a.K, m0, n0);
+  if constexpr (DMA) lg::tile_dma<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.Mx, a.Nx, a.K, m0, n0);
+  else lg::tile_rs<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.M, a.N, a.K, m0, n0);
   const float us = a.hdr->unscale;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -722,13 +727,16 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.M = (int)N;
     b.N = (int)H;
     b.K = (int)V;
+    b.Mx = (int)N;
+    b.Nx = (int)H;
     b.C = (uint16_t*)gh;
     b.ldc = ldgh;
     b.hdr = hdr;
-    auto fn = fast ? lin_bwd_kernel<T, lg::kKC, lg::kKO> : lin_bwd_kernel<T, lg::kKC, lg::kKOg>;
-    if (set_lds(fn, 2 * lg::kStageBytes) != CE_OK) return CE_ERR_HIP;
+    auto fn = fast ? lin_bwd_kernel<T, lg::kKC, lg::kKO, true> : lin_bwd_kernel<T, lg::kKC, lg::kKOg, false>;
+    const int lb = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+    if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
     const int64_t grid = ((N + 255) / 256) * ((H + 255) / 256);
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 2 * lg::kStageBytes, st, b);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lb, st, b);
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   if (gw) {  // dW [V, H] = g^T h: A(v, tok) = g[tok][v], B(h, tok) = h[tok][h]
@@ -740,13 +748,16 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.M = (int)V;
     b.N = (int)H;
     b.K = (int)N;
+    b.Mx = (int)L.ldg;  // g's pad columns (zeros) up to its row stride may load
+    b.Nx = (int)H;
     b.C = (uint16_t*)gw;
     b.ldc = ldgw;
     b.hdr = hdr;
-    auto fn = fast ? lin_bwd_kernel<T, lg::kKO, lg::kKO> : lin_bwd_kernel<T, lg::kKO, lg::kKOg>;
-    if (set_lds(fn, 2 * lg::kStageBytes) != CE_OK) return CE_ERR_HIP;
+    auto fn = fast ? lin_bwd_kernel<T, lg::kKO, lg::kKO, true> : lin_bwd_kernel<T, lg::kKO, lg::kKOg, false>;
+    const int lb = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+    if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
     const int64_t grid = ((V + 255) / 256) * ((H + 255) / 256);
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 2 * lg::kStageBytes, st, b);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lb, st, b);
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   hipLaunchKernelGGL(lin_finish_kernel, dim3(1), dim3(kNT), 0, st, loss_rows, labels, N, V, ignore, n_valid,

@@ -45,6 +45,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kBufFlags);
 }
 
+// Buffer resource words (base, 16 bits of base | stride 0, extent, format)
+// for the inline direct-to-LDS load below.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, bytes, (uint32_t)kBufFlags};
+}
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes at resource
+// offset voff + soff (zeros past the extent) go to LDS byte lds_addr + 16 l.
+// Written as inline assembly so that the compiler does not track it as a
+// pending LDS write: it would otherwise wait for every such load in flight
+// (vmcnt 0) before each transposing LDS read.  The caller orders the loads
+// against the LDS reads with explicit vmcnt waits and workgroup barriers;
+// every operand comes from scalar arithmetic (the "s" constraints fail to
+// assemble otherwise), so no vector-written SGPR feeds the load, and M0 is
+// set one wait state before its use.  No result registers are involved.
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // Chunk swizzle of slab row r (2 bits): rows r and r + 8 of a 16-row group,
 // and every pair of the 8-row groups, land on different chunk slots.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) & 3u) ^ ((r >> 3) & 1u); }
@@ -136,8 +161,139 @@ struct Tile {
   f32x16 acc[4][4];
 };
 
+// Operand layouts.  KC: K-contiguous, row i of the operand at p + i ld
+// (h and W in the logits product, g in dh).  KO: K-outer, element (i, k) at
+// p + k ld + i, the operand's rows contiguous (W in dh, g and h in dW).
+enum { kKC = 0, kKO = 1 };
+
+// KO slabs hold a K step as 32 K rows of the tile's 256 operand rows
+// (512 bytes each, 16 KB), the 16-byte chunks of row k XOR-swizzled by
+// ko_swz(k % 4).  The MFMA operand of lane l (operand row l % 32 of a block,
+// K run 8 (l / 32) .. +7) is then gathered with two transposing reads
+// (ds_read_b64_tr_b16): in each 16-lane group, result lane j takes element
+// j % 4 of the 8-byte chunks addressed by lanes j / 4, j / 4 + 4, + 8, + 12
+// of its group, so source lane q of group g points at operand rows
+// 16 (g % 2) + 4 (q % 4) .. +3 of K row 8 (g / 2) + 4 h + q / 4 (read h
+// gives K elements 4 h .. 4 h + 3 of the run).  The swizzle values keep the
+// four K rows of a 16-lane group, and of a 32-lane half, on distinct banks.
+__device__ __forceinline__ uint32_t ko_swz(uint32_t k4) { return (0xCA60u >> (4 * k4)) & 15u; }  // 0, 6, 10, 12
+
+// One operand's direct-to-LDS loads and MFMA operand reads.
+template <int KIND>
+struct DmaOp;
+
+template <>
+struct DmaOp<kKC> {
+  u32x4 rw;
+  SlabOffsets o;
+  int K;
+  // rows: the operand's extent along M / N from the tile origin
+  __device__ __forceinline__ void init(const char* p, int64_t ld, int origin, int extent, int K_, int wave, int lane) {
+    const int64_t lb = ld * 2;
+    const int rows = extent - origin;
+    rw = rsrc_words(p + (int64_t)origin * lb, (uint32_t)((int64_t)(rows < 256 ? rows : 256) * lb));
+    o = slab_offsets(lb, rows, wave, lane);
+    K = K_;
+  }
+  // instruction i of step kt: slab rows 16 (4 wave + i) .. +15; chunks at or
+  // past K (only in the last step, or in steps past it) load zeros
+  __device__ __forceinline__ void load1(char* slab, int kt, int wave, int i) const {
+    uint32_t off = o.off[i];
+    if ((kt + 1) * BK > K && kt * BK + o.chunk[i] * 8 >= K) off = kOob;
+    dma16(rw, lds_addr_of(slab + (wave * 4 + i) * 1024), off, (uint32_t)kt * (BK * 2));
+  }
+  __device__ __forceinline__ void load(char* slab, int kt, int wave) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load1(slab, kt, wave, i);
+  }
+  // per-step context of the loads (none) and load i of a step
+  __device__ __forceinline__ int ctx(int) const { return 0; }
+  __device__ __forceinline__ void issue(int, char* slab, int kt, int wave, int i) const { load1(slab, kt, wave, i); }
+  // operand of block rows mb .. mb + 31 (relative to the tile), K half kk
+  __device__ __forceinline__ u32x4 frag_of(const char* slab, int mb, int kk, int lane) const {
+    return frag(slab, mb + (lane & 31), kk, lane >> 5);
+  }
+  static constexpr int kReads = 1;  // LDS instructions per operand
+};
+
+template <>
+struct DmaOp<kKO> {
+  const char* base;   // element (origin, 0)
+  int64_t lb;         // bytes between K rows
+  int K;
+  uint32_t full, part;  // extent of a whole step / of the last partial one
+  uint32_t off[4];    // per instruction: byte offset in the step's 32 K rows, or past every extent
+  uint32_t rd;        // per lane: K row and 8-byte half of its first transposing read (kk 0, h 0)
+  uint32_t cx;        // per lane: low chunk bits and swizzle, XORed with a block's chunk base
+  // extent: the operand's rows (columns of the stored matrix) that may be
+  // loaded; whole 16-byte chunks from origin on below it are loaded
+  __device__ __forceinline__ void init(const char* p, int64_t ld, int origin, int extent, int K_, int wave, int lane) {
+    lb = ld * 2;
+    base = p + (int64_t)origin * 2;
+    K = K_;
+    full = (uint32_t)(BK * lb);
+    part = (uint32_t)((K % BK) * lb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 2 * (wave * 4 + i) + (lane >> 5);  // K row of the step
+      const int c = (lane & 31) ^ (int)ko_swz((uint32_t)rr & 3u);
+      off[i] = (origin + 8 * c < extent) ? (uint32_t)((int64_t)rr * lb + c * 16) : kOob;
+    }
+    const int g = lane >> 4, q = lane & 15;
+    const int k = 8 * (g >> 1) + (q >> 2);      // K row of read h = 0 (its row mod 4 is (q / 4) mod 4)
+    const int cl = 2 * (g & 1) + ((q & 3) >> 1);  // chunk within the block's four
+    rd = (uint32_t)(k * 512 + (q & 1) * 8);
+    cx = (uint32_t)cl ^ ko_swz((uint32_t)(q >> 2) & 3u);
+  }
+  // step kt: K rows 32 kt .. 32 kt + 31 through a resource that ends at K,
+  // so rows past K (and every row of a step past the last) load zeros.  The
+  // extent is chosen with scalar selects (a clamp would be a vector op).
+  __device__ __forceinline__ u32x4 step_words(int kt) const {
+    const int kf = K / BK;
+    const uint32_t nrec = kt < kf ? full : (kt == kf ? part : 0u);
+    return rsrc_words(base + (int64_t)kt * BK * lb, nrec);
+  }
+  __device__ __forceinline__ void load1(const u32x4& rw, char* slab, int wave, int i) const {
+    dma16(rw, lds_addr_of(slab + (wave * 4 + i) * 1024), off[i], 0u);
+  }
+  __device__ __forceinline__ void load(char* slab, int kt, int wave) const {
+    const u32x4 rw = step_words(kt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load1(rw, slab, wave, i);
+  }
+  __device__ __forceinline__ u32x4 ctx(int kt) const { return step_words(kt); }
+  __device__ __forceinline__ void issue(const u32x4& rw, char* slab, int, int wave, int i) const {
+    load1(rw, slab, wave, i);
+  }
+  // block rows mb .. mb + 31 (mb a multiple of 32): the lane's chunk is
+  // mb / 8 + cl, whose slot is (mb / 8 + cl) ^ swz = (mb / 8) ^ cx (mb / 8 is a
+  // multiple of 4 and cl < 4, so the sum is an XOR)
+  __device__ __forceinline__ u32x4 frag_of(const char* slab, int mb, int kk, int lane) const {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint32_t a = rd + ((((uint32_t)mb >> 3) ^ cx) << 4) + (uint32_t)kk * (16 * 512);
+    const __attribute__((address_space(3))) char* sl = (const __attribute__((address_space(3))) char*)slab;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sl + a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sl + a + 4 * 512));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+  static constexpr int kReads = 2;
+};
+
 // The wave's eight MFMA operands of half kk of a K step: A rows
 // wm * 128 + i * 32 + lane % 32 and B rows wn * 128 + j * 32 + lane % 32.
+template <int AK, int BKD>
+__device__ __forceinline__ void read_frags(const char* st, const DmaOp<AK>& oa, const DmaOp<BKD>& ob, int wm, int wn,
+                                           int lane, int kk, u32x4 (&a)[4], u32x4 (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = oa.frag_of(st, wm * 128 + i * 32, kk, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = ob.frag_of(st + kSlabBytes, wn * 128 + j * 32, kk, lane);
+}
+
+// The same for two KC slabs (the register-staged loop below).
 __device__ __forceinline__ void read_frags(const char* st, int wm, int wn, int lane, int kk, u32x4 (&a)[4],
                                            u32x4 (&b)[4]) {
 #pragma unroll
@@ -146,89 +302,88 @@ __device__ __forceinline__ void read_frags(const char* st, int wm, int wn, int l
   for (int j = 0; j < 4; ++j) b[j] = frag(st + kSlabBytes, wn * 128 + j * 32 + (lane & 31), kk, lane >> 5);
 }
 
-// The K loop of one 256 x 256 tile: acc = A[m0:, :] B[n0:, :]^T.
-template <typename T>
-__device__ __forceinline__ void tile_nt(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
-                                        int M, int N, int K, int m0, int n0) {
+// The K loop of one 256 x 256 tile: acc = A[m0:, :] B[n0:, :]^T, A and B
+// of layouts AK / BKD (16-byte aligned rows; a KO operand's extent along
+// its tile dimension a whole number of 16-byte chunks or padded to one).
+// Needs kLdsBytes of LDS.
+template <typename T, int AK, int BKD>
+__device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
+                                         int M, int N, int K, int m0, int n0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t la = lda * 2, lb = ldb * 2;
-  // the operands' rows from m0 / n0 on (their extents bound every load)
-  const int rows_a = M - m0, rows_b = N - n0;
-  const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(A + (int64_t)m0 * la, (uint32_t)((int64_t)(rows_a < 256 ? rows_a : 256) * la));
-  const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(B + (int64_t)n0 * lb, (uint32_t)((int64_t)(rows_b < 256 ? rows_b : 256) * lb));
+  DmaOp<AK> oa;
+  DmaOp<BKD> ob;
+  oa.init(A, lda, m0, M, K, wave, lane);
+  ob.init(B, ldb, n0, N, K, wave, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) t.acc[i][j] = f32x16{};
   const int KT = (K + BK - 1) / BK;
-  const SlabOffsets oa = slab_offsets(la, rows_a, wave, lane), ob = slab_offsets(lb, rows_b, wave, lane);
-  // prologue: steps 0..2 in flight, then step 0's first operands
+  // Steps at or past KT load nothing (zero fills of a stage that is never
+  // read for a product).  That keeps the loop body one basic block and the
+  // wait counts fixed.
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < KT) {
-      char* st = lds + s * kStageBytes;
-      load_step(ra, st, oa, s, K, wave);
-      load_step(rb, st + kSlabBytes, ob, s, K, wave);
-    }
+    char* st = lds + s * kStageBytes;
+    oa.load(st, s, wave);
+    ob.load(st + kSlabBytes, s, wave);
   }
-  if (KT >= 3) wait_vm<16>();
-  else if (KT == 2) wait_vm<8>();
-  else wait_vm<0>();
+  wait_vm<16>();  // step 0 (this lane's part)
   lds_barrier();
   u32x4 a0[4], b0[4], a1[4], b1[4];
-  read_frags(lds, wm, wn, lane, 0, a0, b0);
-  // Rotated pipeline.  Step kt, first half: its products on (a0, b0) with the
-  // reads of its second-half operands (a1, b1) between them.  Then the
-  // barrier for step kt + 1 (every lane's loads of it have landed, and every
-  // lane has finished reading step kt - 1, whose buffer is free).  Second
-  // half: its products on (a1, b1) with, between them, the loads of step
-  // kt + 3 into step kt - 1's buffer and the reads of step kt + 1's first
-  // operands.  Three steps of loads stay in flight.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a0[i] = oa.frag_of(lds, wm * 128 + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b0[j] = ob.frag_of(lds + kSlabBytes, wn * 128 + j * 32, 0, lane);
+  // Rotated pipeline, one wave per SIMD, its instruction order fixed by
+  // scheduling fences.  Step kt, first half: the 16 products on (a0, b0),
+  // the first eight each preceded by one read of the second-half operands
+  // (a1, b1).  Then the barrier for step kt + 1 (every lane's loads of it
+  // have landed, and every lane has consumed step kt - 1, whose stage is
+  // free).  Second half: the 16 products on (a1, b1), preceded by the eight
+  // reads of step kt + 1's first operands and then by the eight loads of
+  // step kt + 3 into step kt - 1's stage (reads before loads: both touch
+  // LDS).  Each half starts by waiting for the reads of the half before
+  // (long landed by then), so no product waits on a read just issued.
   for (int kt = 0; kt < KT; ++kt) {
     const char* st = lds + (kt % STAGES) * kStageBytes;
-    read_frags(st, wm, wn, lane, 1, a1, b1);
+    wait_lgkm0();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) t.acc[i][j] = Mfma<T>::run(a0[i], b0[j], t.acc[i][j]);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one operand read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two products
+    for (int s = 0; s < 16; ++s) {
+      if (s < 4) a1[s] = oa.frag_of(st, wm * 128 + s * 32, 1, lane);
+      else if (s < 8) b1[s - 4] = ob.frag_of(st + kSlabBytes, wn * 128 + (s - 4) * 32, 1, lane);
+      t.acc[s >> 2][s & 3] = Mfma<T>::run(a0[s >> 2], b0[s & 3], t.acc[s >> 2][s & 3]);
+      sched_fence();
     }
-    sched_fence();
-    if (kt + 1 < KT) {
-      if (kt + 3 <= KT) wait_vm<8>();
-      else wait_vm<0>();
-      __builtin_amdgcn_s_barrier();
-    }
-    sched_fence();
-    if (kt + 3 < KT) {
-      char* nx = lds + ((kt + 3) % STAGES) * kStageBytes;
-      load_step(ra, nx, oa, kt + 3, K, wave);
-      load_step(rb, nx + kSlabBytes, ob, kt + 3, K, wave);
-    }
-    if (kt + 1 < KT) read_frags(lds + ((kt + 1) % STAGES) * kStageBytes, wm, wn, lane, 0, a0, b0);
+    wait_vm<8>();  // step kt + 1 (the eight newest loads are step kt + 2's)
+    __builtin_amdgcn_s_barrier();
+    wait_lgkm0();
+    const char* s1 = lds + ((kt + 1) % STAGES) * kStageBytes;
+    char* nx = lds + ((kt + 3) % STAGES) * kStageBytes;
+    const auto ca = oa.ctx(kt + 3);
+    const auto cb = ob.ctx(kt + 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) t.acc[i][j] = Mfma<T>::run(a1[i], b1[j], t.acc[i][j]);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one K-step load
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+    for (int s = 0; s < 16; ++s) {
+      if (s < 4) a0[s] = oa.frag_of(s1, wm * 128 + s * 32, 0, lane);
+      else if (s < 8) b0[s - 4] = ob.frag_of(s1 + kSlabBytes, wn * 128 + (s - 4) * 32, 0, lane);
+      else if (s < 12) oa.issue(ca, nx, kt + 3, wave, s - 8);
+      else ob.issue(cb, nx + kSlabBytes, kt + 3, wave, s - 12);
+      t.acc[s >> 2][s & 3] = Mfma<T>::run(a1[s >> 2], b1[s & 3], t.acc[s >> 2][s & 3]);
+      sched_fence();
     }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one operand read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-    }
-    sched_fence();
   }
+  // the zero-fill loads of the steps past KT and the last reads are drained
+  // before the caller reuses the LDS
+  wait_vm<0>();
+  wait_lgkm0();
+}
+
+template <typename T>
+__device__ __forceinline__ void tile_nt(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
+                                        int M, int N, int K, int m0, int n0) {
+  tile_dma<T, kKC, kKC>(t, lds, A, lda, B, ldb, M, N, K, m0, n0);
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +398,6 @@ __device__ __forceinline__ void tile_nt(Tile& t, char* lds, const char* A, int64
 // step earlier) goes to LDS and the loads of step kt + 2 refill it; LDS holds
 // two steps.
 // ---------------------------------------------------------------------------
-enum { kKC = 0, kKO = 1 };
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Stage {
