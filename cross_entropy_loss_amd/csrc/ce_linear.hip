@@ -474,6 +474,10 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
 // ---------------------------------------------------------------------------
 // 3-4. dh = g W and dW = g^T h (16-bit): MFMA tiles, 2^-k on output.
 // ---------------------------------------------------------------------------
+// LDS of the direct-to-LDS backward kernels: the K loop's stages, then the
+// epilogue's four 128 x 136 staged quarters
+constexpr int kBwdLds = (lg::kLdsBytes > 4 * 128 * 136 * 2) ? lg::kLdsBytes : 4 * 128 * 136 * 2;
+
 struct BwdArgs {
   const char* A;
   int64_t lda;
@@ -483,6 +487,7 @@ struct BwdArgs {
   int Mx, Nx;  // loadable extents along M / N (at least M / N)
   uint16_t* C;
   int64_t ldc;
+  int vec_out;  // C 16-byte aligned, ldc and N multiples of 8
   const LinHeader* hdr;
 };
 
@@ -494,13 +499,46 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int mt = (a.M + 255) / 256, nt = (a.N + 255) / 256;
   int mti, nti;
-  lg::tile_of(blockIdx.x, mt, nt, mti, nti);
+  // g (the A operand of both products) is the larger operand: its tiles are
+  // shared within an XCD
+  lg::tile_of_rows(blockIdx.x, mt, nt, mti, nti);
   const int m0 = mti * 256, n0 = nti * 256;
   Tile t;
   if constexpr (DMA) lg::tile_dma<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.Mx, a.Nx, a.K, m0, n0);
   else lg::tile_rs<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.M, a.N, a.K, m0, n0);
   const float us = a.hdr->unscale;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  if constexpr (DMA) {
+    // Each wave stages its 128 x 128 quarter in LDS (rows of 272 bytes) and
+    // writes it out as 16-byte vectors (8 elements; a.vec_out: C 16-byte
+    // aligned with whole vectors per row), else element by element.
+    constexpr int kGS = 136;
+    __syncthreads();  // every wave is done with the K loop's LDS
+    uint16_t* stg = (uint16_t*)(lds + wave * (128 * kGS * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          stg[lg::acc_row(0, i, v, lane) * kGS + lg::acc_col(0, j, lane)] = to_bits<T>(t.acc[i][j][v] * us);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+    const int cb = n0 + wn * 128;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int rr = q * 4 + (lane >> 4), cv = (lane & 15) * 8;
+      const int R = m0 + wm * 128 + rr, c = cb + cv;
+      if (R >= a.M || c >= a.N) continue;
+      uint16_t* dst = a.C + (int64_t)R * a.ldc + c;
+      const uint16_t* src = stg + rr * kGS + cv;
+      if (a.vec_out) {
+        *(lg::u32x4*)dst = *(const lg::u32x4*)src;
+      } else {
+        for (int e = 0; e < 8 && c + e < a.N; ++e) dst[e] = src[e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -731,9 +769,10 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.Nx = (int)H;
     b.C = (uint16_t*)gh;
     b.ldc = ldgh;
+    b.vec_out = aligned16(gh, ldgh, 2) && H % 8 == 0;
     b.hdr = hdr;
     auto fn = fast ? lin_bwd_kernel<T, lg::kKC, lg::kKO, true> : lin_bwd_kernel<T, lg::kKC, lg::kKOg, false>;
-    const int lb = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+    const int lb = fast ? kBwdLds : 2 * lg::kStageBytes;
     if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
     const int64_t grid = ((N + 255) / 256) * ((H + 255) / 256);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lb, st, b);
@@ -752,9 +791,10 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.Nx = (int)H;
     b.C = (uint16_t*)gw;
     b.ldc = ldgw;
+    b.vec_out = aligned16(gw, ldgw, 2) && H % 8 == 0;
     b.hdr = hdr;
     auto fn = fast ? lin_bwd_kernel<T, lg::kKO, lg::kKO, true> : lin_bwd_kernel<T, lg::kKO, lg::kKOg, false>;
-    const int lb = fast ? lg::kLdsBytes : 2 * lg::kStageBytes;
+    const int lb = fast ? kBwdLds : 2 * lg::kStageBytes;
     if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
     const int64_t grid = ((V + 255) / 256) * ((H + 255) / 256);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lb, st, b);

@@ -328,9 +328,9 @@ __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int6
   for (int s = 0; s < STAGES - 1; ++s) {
     char* st = lds + s * kStageBytes;
     oa.load(st, s, wave);
-    ob.load(st + kSlabBytes, s, wave);
+    if (s < STAGES - 2) ob.load(st + kSlabBytes, s, wave);  // step 2's B loads go out in step 0
   }
-  wait_vm<16>();  // step 0 (this lane's part)
+  wait_vm<12>();  // step 0 (this lane's part)
   lds_barrier();
   u32x4 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
@@ -340,36 +340,40 @@ __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int6
   // Rotated pipeline, one wave per SIMD, its instruction order fixed by
   // scheduling fences.  Step kt, first half: the 16 products on (a0, b0),
   // the first eight each preceded by one read of the second-half operands
-  // (a1, b1).  Then the barrier for step kt + 1 (every lane's loads of it
-  // have landed, and every lane has consumed step kt - 1, whose stage is
-  // free).  Second half: the 16 products on (a1, b1), preceded by the eight
-  // reads of step kt + 1's first operands and then by the eight loads of
-  // step kt + 3 into step kt - 1's stage (reads before loads: both touch
-  // LDS).  Each half starts by waiting for the reads of the half before
-  // (long landed by then), so no product waits on a read just issued.
+  // (a1, b1), the next four by the B loads of step kt + 2 (into the stage of
+  // step kt - 2, free since the last barrier).  Then the barrier for step
+  // kt + 1 (every lane's loads of it have landed, and every lane has
+  // consumed step kt - 1, whose stage is free).  Second half: the 16
+  // products on (a1, b1), preceded by the eight reads of step kt + 1's
+  // first operands and then by the A loads of step kt + 3 into step kt - 1's
+  // stage (reads before loads: both touch LDS).  The two halves' loads keep
+  // the four waves from flooding the address unit at once.  Each half
+  // starts by waiting for the reads of the half before (long landed by
+  // then), so no product waits on a read just issued.
   for (int kt = 0; kt < KT; ++kt) {
     const char* st = lds + (kt % STAGES) * kStageBytes;
+    char* n2 = lds + ((kt + 2) % STAGES) * kStageBytes + kSlabBytes;
+    const auto cb = ob.ctx(kt + 2);
     wait_lgkm0();
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4) a1[s] = oa.frag_of(st, wm * 128 + s * 32, 1, lane);
       else if (s < 8) b1[s - 4] = ob.frag_of(st + kSlabBytes, wn * 128 + (s - 4) * 32, 1, lane);
+      else if (s < 12) ob.issue(cb, n2, kt + 2, wave, s - 8);
       t.acc[s >> 2][s & 3] = Mfma<T>::run(a0[s >> 2], b0[s & 3], t.acc[s >> 2][s & 3]);
       sched_fence();
     }
-    wait_vm<8>();  // step kt + 1 (the eight newest loads are step kt + 2's)
+    wait_vm<8>();  // step kt + 1 (the eight newest loads: B of step kt + 2, A of step kt + 2)
     __builtin_amdgcn_s_barrier();
     wait_lgkm0();
     const char* s1 = lds + ((kt + 1) % STAGES) * kStageBytes;
     char* nx = lds + ((kt + 3) % STAGES) * kStageBytes;
     const auto ca = oa.ctx(kt + 3);
-    const auto cb = ob.ctx(kt + 3);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4) a0[s] = oa.frag_of(s1, wm * 128 + s * 32, 0, lane);
       else if (s < 8) b0[s - 4] = ob.frag_of(s1 + kSlabBytes, wn * 128 + (s - 4) * 32, 0, lane);
       else if (s < 12) oa.issue(ca, nx, kt + 3, wave, s - 8);
-      else ob.issue(cb, nx + kSlabBytes, kt + 3, wave, s - 12);
       t.acc[s >> 2][s & 3] = Mfma<T>::run(a1[s >> 2], b1[s & 3], t.acc[s >> 2][s & 3]);
       sched_fence();
     }
@@ -637,6 +641,22 @@ __device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& m_tile, in
   } else {
     n_tile = bid / mt;
     m_tile = bid % mt;
+  }
+}
+
+// The same with each XCD walking whole rows of column tiles: the nt column
+// tiles that share one A tile run on one XCD (for products whose A operand
+// is the larger one).
+__device__ __forceinline__ void tile_of_rows(int bid, int mt, int nt, int& m_tile, int& n_tile) {
+  const int total = mt * nt;
+  const int x = bid & 7, q = bid >> 3;
+  if ((total & 7) == 0) {
+    const int lin = x * (total >> 3) + q;
+    m_tile = lin / nt;
+    n_tile = lin % nt;
+  } else {
+    m_tile = bid / nt;
+    n_tile = bid % nt;
   }
 }
 
