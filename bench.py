@@ -134,7 +134,9 @@ def _db_rows(path, sql):
 def profile_summary_linear(d: str, workload: int) -> None:
     """Kernel-trace summary of the LM-head path (bench.py --op linear) ->
     profiles/ce_linear_<workload>.txt: per kernel the time per call, and for
-    the GEMMs their rate over 2 N H V flops each."""
+    the three matrix-product kernels (logits + cross-entropy epilogue, dh,
+    dW) their rate over 2 N H V flops each.  The two backward launches of a
+    call are told apart by their order (dh, then dW)."""
     import glob
     import workloads as wl
     workload = workload if workload in wl.LINEAR_WORKLOADS else 1
@@ -142,9 +144,27 @@ def profile_summary_linear(d: str, workload: int) -> None:
     trace = (glob.glob(os.path.join(d, "**", "trace_results.db"), recursive=True) or [None])[0]
     if not trace:
         raise SystemExit(f"no trace_results.db under {d}")
-    calls = _db_rows(trace, "select count(*) from kernels where name like '%lin_prep_kernel%'")[0][0]
-    rows = _db_rows(trace, "select name, count(*), sum(duration), avg(duration) from kernels "
-                           "group by name order by sum(duration) desc")
+    rows = _db_rows(trace, "select name, duration from kernels order by start")
+    calls = sum(1 for n, _ in rows if "lin_prep_kernel" in n)
+    per = {}
+    bwd_seen = 0
+    for name, dur in rows:
+        if name.startswith(("void at::native", "__amd_rocclr", "cek::ws_fill")):
+            continue  # the benchmark's own flush / copies, the workspace fill
+        if "lin_prep_kernel" in name:
+            bwd_seen = 0
+            label = "lin_prep_kernel (labels, counts)"
+        elif "lin_logits_ce_kernel" in name:
+            label = "lin_logits_ce_kernel (logits = h W^T + cross-entropy epilogue, all chunks)"
+        elif "lin_bwd_kernel" in name:
+            label = ("lin_bwd_kernel dh = g W" if bwd_seen == 0 else "lin_bwd_kernel dW = g^T h")
+            bwd_seen += 1
+        elif "lin_finish_kernel" in name:
+            label = "lin_finish_kernel (token mean, status)"
+        else:
+            label = name[:72]
+        n, s_ = per.get(label, (0, 0))
+        per[label] = (n + 1, s_ + dur)
     flops_per_gemm = 2.0 * lw.N * lw.H * lw.V
     lines = [f"# rocprofv3 summary: LM-head projection + cross-entropy (ce_linear_fwd_bwd), workload {lw.name}",
              f"# N={lw.N} H={lw.H} V={lw.V} dtype={lw.dtype} chunk_rows={lw.chunk_rows or 'default'}",
@@ -152,19 +172,17 @@ def profile_summary_linear(d: str, workload: int) -> None:
              "#   rocprofv3 --kernel-trace --stats -d D -o trace -- "
              f"python bench.py --op linear --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
              f"#   python bench.py --op linear --profile-summary D --workload {workload}", "",
-             f"{calls} calls traced; per call:",
-             f"  {'kernel':72s} {'launches':>8s} {'ms/call':>9s} {'TFLOP/s':>8s}"]
+             f"{calls} calls traced (the first ones warm-up); per call:",
+             f"  {'kernel':76s} {'launches':>8s} {'ms/call':>9s} {'TFLOP/s':>8s}"]
     total = 0.0
-    for name, n, s, a in rows:
-        if name.startswith(("void at::native", "__amd_rocclr", "cek::ws_fill")):
-            continue  # the benchmark's own flush / copies, the workspace fill
-        per_call = s / calls / 1e6
+    for label, (n, s_) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        per_call = s_ / calls / 1e6
         total += per_call
         rate = ""
-        if name.startswith(("Cijk_", "Custom_Cijk_")):  # the library GEMMs (Tensile kernel names)
+        if label.startswith(("lin_logits_ce_kernel", "lin_bwd_kernel")):
             rate = f"{flops_per_gemm / (per_call * 1e-3) / 1e12:8.0f}"
-        lines.append(f"  {name[:72]:72s} {n // calls:8d} {per_call:9.3f} {rate:>8s}")
-    lines.append(f"  {'total':72s} {'':8s} {total:9.3f} {3 * flops_per_gemm / (total * 1e-3) / 1e12:8.0f}")
+        lines.append(f"  {label:76s} {n // calls:8d} {per_call:9.3f} {rate:>8s}")
+    lines.append(f"  {'total':76s} {'':8s} {total:9.3f} {3 * flops_per_gemm / (total * 1e-3) / 1e12:8.0f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"ce_linear_{lw.name}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")

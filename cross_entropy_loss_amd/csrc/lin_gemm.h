@@ -306,9 +306,10 @@ __device__ __forceinline__ void read_frags(const char* st, int wm, int wn, int l
 // of layouts AK / BKD (16-byte aligned rows; a KO operand's extent along
 // its tile dimension a whole number of 16-byte chunks or padded to one).
 // Needs kLdsBytes of LDS.
-template <typename T, int AK, int BKD>
+template <typename T, int AK, int BKD, int S = STAGES>
 __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
                                          int M, int N, int K, int m0, int n0) {
+  static_assert(S >= 4, "the loads of a step go out two and three steps ahead");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -325,55 +326,56 @@ __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int6
   // read for a product).  That keeps the loop body one basic block and the
   // wait counts fixed.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
+  for (int s = 0; s < S - 1; ++s) {
     char* st = lds + s * kStageBytes;
     oa.load(st, s, wave);
-    if (s < STAGES - 2) ob.load(st + kSlabBytes, s, wave);  // step 2's B loads go out in step 0
+    if (s < S - 2) ob.load(st + kSlabBytes, s, wave);  // step S - 2's B loads go out in step 0
   }
-  wait_vm<12>();  // step 0 (this lane's part)
+  wait_vm<(S - 3) * 8 + 4>();  // step 0 (this lane's part)
   lds_barrier();
   u32x4 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) a0[i] = oa.frag_of(lds, wm * 128 + i * 32, 0, lane);
 #pragma unroll
   for (int j = 0; j < 4; ++j) b0[j] = ob.frag_of(lds + kSlabBytes, wn * 128 + j * 32, 0, lane);
-  // Rotated pipeline, one wave per SIMD, its instruction order fixed by
-  // scheduling fences.  Step kt, first half: the 16 products on (a0, b0),
-  // the first eight each preceded by one read of the second-half operands
-  // (a1, b1), the next four by the B loads of step kt + 2 (into the stage of
-  // step kt - 2, free since the last barrier).  Then the barrier for step
-  // kt + 1 (every lane's loads of it have landed, and every lane has
-  // consumed step kt - 1, whose stage is free).  Second half: the 16
-  // products on (a1, b1), preceded by the eight reads of step kt + 1's
-  // first operands and then by the A loads of step kt + 3 into step kt - 1's
-  // stage (reads before loads: both touch LDS).  The two halves' loads keep
-  // the four waves from flooding the address unit at once.  Each half
-  // starts by waiting for the reads of the half before (long landed by
-  // then), so no product waits on a read just issued.
+  // Rotated pipeline over S stages, one wave per SIMD, its instruction
+  // order fixed by scheduling fences.  Step kt, first half: the 16 products
+  // on (a0, b0), the first eight each preceded by one read of the
+  // second-half operands (a1, b1), the next four by the B loads of step
+  // kt + S - 2 (into the stage of step kt - 2, free since the last
+  // barrier).  Then the barrier for step kt + 1 (every lane's loads of it
+  // have landed, and every lane has consumed step kt - 1, whose stage is
+  // free).  Second half: the 16 products on (a1, b1), preceded by the eight
+  // reads of step kt + 1's first operands and then by the A loads of step
+  // kt + S - 1 into step kt - 1's stage (reads before loads: both touch
+  // LDS).  The two halves' loads keep the four waves from flooding the
+  // address unit at once.  Each half starts by waiting for the reads of the
+  // half before (long landed by then), so no product waits on a read just
+  // issued.
   for (int kt = 0; kt < KT; ++kt) {
-    const char* st = lds + (kt % STAGES) * kStageBytes;
-    char* n2 = lds + ((kt + 2) % STAGES) * kStageBytes + kSlabBytes;
-    const auto cb = ob.ctx(kt + 2);
+    const char* st = lds + (kt % S) * kStageBytes;
+    char* n2 = lds + ((kt + S - 2) % S) * kStageBytes + kSlabBytes;
+    const auto cb = ob.ctx(kt + S - 2);
     wait_lgkm0();
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4) a1[s] = oa.frag_of(st, wm * 128 + s * 32, 1, lane);
       else if (s < 8) b1[s - 4] = ob.frag_of(st + kSlabBytes, wn * 128 + (s - 4) * 32, 1, lane);
-      else if (s < 12) ob.issue(cb, n2, kt + 2, wave, s - 8);
+      else if (s < 12) ob.issue(cb, n2, kt + S - 2, wave, s - 8);
       t.acc[s >> 2][s & 3] = Mfma<T>::run(a0[s >> 2], b0[s & 3], t.acc[s >> 2][s & 3]);
       sched_fence();
     }
-    wait_vm<8>();  // step kt + 1 (the eight newest loads: B of step kt + 2, A of step kt + 2)
+    wait_vm<(S - 3) * 8>();  // step kt + 1 (the newer loads: steps kt + 2 .. kt + S - 2)
     __builtin_amdgcn_s_barrier();
     wait_lgkm0();
-    const char* s1 = lds + ((kt + 1) % STAGES) * kStageBytes;
-    char* nx = lds + ((kt + 3) % STAGES) * kStageBytes;
-    const auto ca = oa.ctx(kt + 3);
+    const char* s1 = lds + ((kt + 1) % S) * kStageBytes;
+    char* nx = lds + ((kt + S - 1) % S) * kStageBytes;
+    const auto ca = oa.ctx(kt + S - 1);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4) a0[s] = oa.frag_of(s1, wm * 128 + s * 32, 0, lane);
       else if (s < 8) b0[s - 4] = ob.frag_of(s1 + kSlabBytes, wn * 128 + (s - 4) * 32, 0, lane);
-      else if (s < 12) oa.issue(ca, nx, kt + 3, wave, s - 8);
+      else if (s < 12) oa.issue(ca, nx, kt + S - 1, wave, s - 8);
       t.acc[s >> 2][s & 3] = Mfma<T>::run(a1[s >> 2], b1[s & 3], t.acc[s >> 2][s & 3]);
       sched_fence();
     }
