@@ -203,26 +203,43 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
 
 /*
  * LM-head projection followed by the cross-entropy above, forward and
- * backward, token-chunked.  The pages compare the plain kernel with a fused
- * linear cross-entropy (PyPI page "fms-acceleration-foak 0.7.4", "Running
- * Liger Kernel Benchmarks"), list fused cross-entropy among the kernels to
- * come (fms-hf-tuning PR #280, "Notes on FastKernels") and leave a chunked
- * loss as a to-do (fms-acceleration PR #79, "TODO").  With hidden states
+ * backward.  The pages compare the plain kernel with a fused linear
+ * cross-entropy (PyPI page "fms-acceleration-foak 0.7.4", "Running Liger
+ * Kernel Benchmarks"), list fused cross-entropy among the kernels to come
+ * (fms-hf-tuning PR #280, "Notes on FastKernels") and leave a chunked loss as
+ * a to-do (fms-acceleration PR #79, "TODO").  With hidden states
  * h [n_rows, hidden_size] and the weight W [vocab, hidden_size] of a bias-free
  * linear layer:
  *
- *   logits      = h W^T          (fp32, never stored beyond chunk_rows rows)
+ *   logits      = h W^T
  *   L, loss_rows, n_valid, status  as ce_forward on those logits
  *   grad_hidden = g W,  grad_weight = g^T h,  g = dloss * dL/dlogits
  *
- * Rows are processed chunk_rows at a time (0 = 1024; rounded up to a multiple
- * of 64, and up so that there are at most 4096 chunks): the chunk's logits by
- * a library GEMM (rocBLAS: inputs in dtype, fp32 accumulation, fp32 result),
- * its loss and gradient by the kernels of ce_fwd_bwd_inplace on those fp32
- * logits (fp64 arithmetic) with the token mean over the whole batch, the
- * gradient rounded to dtype (bf16 / fp16) for the two backward GEMMs (fp32
- * accumulation); grad_weight is accumulated in fp32 over the chunks and
- * rounded once to dtype at the end.
+ * bf16 / fp16: every product runs on the matrix cores of this library's own
+ * kernels (16-bit inputs, fp32 accumulation, no other library).  The logits
+ * are never stored: each 256 x 256 tile of them stays in the registers of
+ * the workgroup that computed it, whose epilogue takes per row the tile's
+ * max and label-excluded sum of exponentials (fp32), merges them with the
+ * row's other vocabulary tiles through the workspace (a bounded wait; on
+ * expiry CE_STATUS_SYNC_TIMEOUT and NaN results), writes loss_rows (fp32:
+ * lse - x_y, or log1p(S / e^{x_y}) when p_y > 1/2) and turns the tile into
+ * its part of g, rounded once to dtype.  All tiles of a chunk of rows are
+ * resident at once (a cooperative launch): 256 floor(CUs / ceil(vocab / 256))
+ * rows per chunk (512 with vocab 32000 on 256 CUs; chunk_rows is not used).
+ * g is held scaled by 2^k (k = 0 for bf16; for fp16, k puts dloss / n_valid
+ * near 2^14 so that g stays in range) and the two backward products remove
+ * the scale before rounding grad_hidden and grad_weight once to dtype.
+ * Sums are in a fixed order: repeated calls give identical bits.
+ * Fast operand loads (16-byte direct-to-LDS) need hidden and weight rows
+ * 16-byte aligned (pointer and ld * element size) and hidden_size a multiple
+ * of 8; other layouts load element by element (same results, slower).
+ * vocab above 256 x CUs (65536 on MI355X) gives CE_ERR_UNSUPPORTED.
+ * fp32: chunk_rows rows at a time (0 = 1024; rounded up to a multiple of 64,
+ * and up so that there are at most 4096 chunks): the chunk's fp32 logits by
+ * an fp32 tiled product, its loss and gradient by the kernels of
+ * ce_fwd_bwd_inplace (fp64 arithmetic) with the token mean over the whole
+ * batch, then the two backward products in fp32 (grad_weight accumulated
+ * over the chunks in place).
  *   hidden        n_rows rows of hidden_size elements of dtype, row i at
  *                 i * ld_hidden (ld_hidden >= hidden_size).
  *   weight        vocab rows of hidden_size elements, row v at v * ld_weight.
@@ -233,24 +250,19 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  *   grad_weight   out or NULL: vocab rows, stride ld_grad_weight (all zeros when
  *                 n_rows == 0).
  *   workspace     ce_linear_workspace_bytes(...) bytes, 256-byte aligned,
- *                 prepared once with ce_workspace_init: the cross-entropy
- *                 workspace of a chunk, a chunk of fp32 logits and, for
- *                 bf16/fp16, the chunk's rounded gradient, the fp32
- *                 grad_weight accumulator (vocab x hidden_size x 4 bytes,
- *                 several chunks only) and, when n_rows, hidden_size and vocab
- *                 are multiples of 64, transposed copies of the chunk's
- *                 gradient and hidden rows for the weight-gradient GEMM.
- * GEMMs: hipBLASLt for bf16 / fp16 (its first heuristic algorithm among those
- * needing no workspace), rocBLAS for fp32 and for shapes hipBLASLt has no
- * algorithm for; both accumulate in fp32 without atomics (repeated calls give
- * identical results).
- * Memory: apart from the workspace, rocBLAS and hipBLASLt keep one handle per
- * device for the process lifetime (with the memory they allocate for
- * themselves), and the GEMM descriptors chosen per shape are kept on the host;
- * calls on one device are serialised on the host around those handles.
+ *                 zeroed once with ce_workspace_init and then owned by this
+ *                 function (calls on one workspace must not overlap, and it
+ *                 is not shared with the cross-entropy entry points).
+ *                 bf16 / fp16: a 256-byte header (the call's epoch, scale and
+ *                 status), g (n_rows x vocab rounded up to 8, dtype), the
+ *                 per-row tile statistics of the largest chunk and three
+ *                 n_rows x 8-byte exchange arrays (label logit, lse,
+ *                 1 - p_y).  fp32: a chunk's cross-entropy workspace, the
+ *                 chunk's fp32 logits and per-chunk counts.
  * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
- * dimension of 2^31 or more give CE_ERR_UNSUPPORTED (the GEMMs take 32-bit
- * sizes); a failed GEMM gives CE_ERR_HIP.
+ * dimension of 2^31 or more, or operands whose byte extent reaches 2^31
+ * (the loads use 32-bit buffer offsets), give CE_ERR_UNSUPPORTED; a failed
+ * launch gives CE_ERR_HIP.
  */
 size_t ce_linear_workspace_bytes(int64_t n_rows, int64_t hidden_size, int64_t vocab, int64_t chunk_rows,
                                  int dtype);

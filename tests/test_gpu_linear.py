@@ -141,14 +141,15 @@ def check(out, h, w, y, dtype, dloss=1.0, expect_status=0):
     return ref
 
 
-# vocab a multiple of 4 takes the one-kernel fp32 -> bf16/fp16 gradient step; 3001 / 2999 the in-place
-# fp32 step followed by a cast
+# 16-bit cases run the matrix-core path (logits tiles with the cross-entropy epilogue, then dh and dW);
+# vocab 3001 / 2999 leave a partial 16-byte chunk at the end of g's rows; chunk_rows only matters for fp32.
+# The 16-bit path takes 256 floor(CUs / ceil(V / 256)) rows per cooperative chunk: N = 1100 at V = 32000
+# (512-row chunks on 256 CUs) and N = 600 at V = 40000 (256-row chunks) span three chunks, the last ragged.
 CASES = [("bf16", 256, 384, 3000, 0), ("bf16", 300, 256, 5000, 128), ("f16", 200, 320, 4000, 64),
          ("f32", 130, 192, 2500, 64), ("bf16", 64, 128, 32000, 0), ("bf16", 513, 512, 1000, 256),
          ("bf16", 150, 192, 3001, 64), ("f16", 140, 160, 2999, 64),
-         # rows, hidden and vocab multiples of 64: the weight gradient from transposed operands (TN GEMM),
-         # one chunk and several
-         ("bf16", 256, 256, 4096, 0), ("bf16", 320, 192, 2048, 128), ("f16", 192, 256, 3072, 64)]
+         ("bf16", 256, 256, 4096, 0), ("bf16", 320, 192, 2048, 128), ("f16", 192, 256, 3072, 64),
+         ("bf16", 1100, 128, 32000, 0), ("f16", 600, 64, 40000, 0)]
 
 
 @pytest.mark.parametrize("dtype,N,H,V,chunk", CASES, ids=[f"{d}-N{n}-H{h}-V{v}-c{c}" for d, n, h, v, c in CASES])
@@ -166,8 +167,8 @@ def test_linear_strided_and_dloss():
 
 @pytest.mark.parametrize("ldh", [136, 131])
 def test_linear_tn_strided_hidden(ldh):
-    # shapes that tile by 64: a hidden row stride that keeps 16-byte rows takes the weight gradient from
-    # transposed operands (TN GEMM), one that does not takes the NT form on the stored operands
+    # a hidden row stride that keeps 16-byte rows takes the direct-to-LDS operand loads; one that does not
+    # (131 elements) takes the element-wise loads of the same kernels
     h, w, y = make(26, 128, 128, 2048, "bf16")
     check(run(h, w, y, "bf16", chunk_rows=64, ldh=ldh), h, w, y, "bf16")
 
@@ -207,3 +208,14 @@ def test_linear_deterministic():
     b = run(h, w, y, "bf16", chunk_rows=64)
     for k in ("loss_rows", "grad_hidden", "grad_weight"):
         assert torch.equal(a[k], b[k]), k
+
+
+def test_linear_vocab_beyond_resident_tiles():
+    # 16-bit: every vocabulary tile of a row tile must be resident at once (256 CUs x 256 columns)
+    N, H, V = 16, 64, 65537
+    h, w, y = make(27, N, H, V, "bf16")
+    hd, wd = to_dev(h, "bf16"), to_dev(w, "bf16")
+    yd = torch.from_numpy(np.ascontiguousarray(y)).cuda()
+    with pytest.raises(ce._lib.CeError) as e:
+        ce.ce_linear_fwd_bwd(hd, wd, yd)
+    assert e.value.code == ce._lib.CE_ERR_UNSUPPORTED
