@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ce_api.hip")
 SRCS = [SRC] + [os.path.join(HERE, "csrc", f) for f in ("ce_linear.hip", "rmsnorm.hip", "rope.hip")]
-HEADERS = ("ce_kernels.h", "ce_buffer.h", "ce_internal.h", "row_formats.h", "lin_gemm.h")
+HEADERS = ("ce_kernels.h", "ce_buffer.h", "row_formats.h", "lin_gemm.h")
 DEPS = SRCS + [os.path.join(HERE, "csrc", h) for h in HEADERS] + [os.path.join(ROOT, "include", "ce_mi355x.h")]
 LIBS: list = []  # no libraries beyond the HIP runtime
 LIB = os.path.join(HERE, "libce_mi355x.so")

@@ -8,7 +8,6 @@
 #include <atomic>
 #include <mutex>
 
-#include "ce_internal.h"
 #include "ce_kernels.h"
 #include "ce_mi355x.h"
 
@@ -216,15 +215,6 @@ KernelFn slabgrad_fn(Cfg c) {
   return nullptr;
 }
 
-template <typename TO>
-KernelFn f32to16_fn(Cfg c) {
-#define MAKE(NT, VPL) \
-  if (c.nt == NT && c.vpl == VPL) return cek::row_f32_to16_kernel<TO, NT, VPL, kPol>;
-  CE_CFG_CASES(MAKE)
-#undef MAKE
-  return nullptr;
-}
-
 constexpr int kGradNT = 256, kGradVPL = 4;  // backward slab: 1024 vectors
 KernelFn grad_fn(int dtype) {
   if (dtype == CE_DTYPE_BF16) return cek::grad_kernel<cek::BF16, kGradNT, kGradVPL, kPol>;
@@ -407,35 +397,6 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
   if (rc != CE_OK) return rc;
   return run_forward(true, logits, ld, labels, n_rows, vocab, dtype, ignore_index, chunk, dloss, loss_mean,
                      loss_rows, lse_rows, pcomp_rows, n_valid, status, ws, kScratchBytes, (hipStream_t)stream);
-}
-
-int ce_lin_chunk_f32_to16(const float* logits, int64_t ld, const int64_t* labels, int64_t N, int64_t V,
-                          int out_dtype, int64_t ignore_index, const float* dloss, float* loss_mean, float* loss_rows,
-                          int32_t* n_valid, uint32_t* status, void* grad, int64_t grad_ld, void* ws,
-                          size_t ws_bytes, hipStream_t st) {
-  if (out_dtype != CE_DTYPE_BF16 && out_dtype != CE_DTYPE_F16) return CE_ERR_UNSUPPORTED;
-  if (N <= 0 || V < 1 || V > max_slab(CE_DTYPE_F32) || ld < V || grad_ld < V) return CE_ERR_UNSUPPORTED;
-  if (V % 4 || (uintptr_t)logits % 16 || (ld * 4) % 16 || (uintptr_t)grad % 8 || (grad_ld * 2) % 8)
-    return CE_ERR_UNSUPPORTED;
-  if (labels == nullptr || loss_mean == nullptr || loss_rows == nullptr || n_valid == nullptr)
-    return CE_ERR_INVALID_ARG;
-  Split sp;
-  if (!make_split(V, 0, CE_DTYPE_F32, &sp) || sp.C != 1) return CE_ERR_UNSUPPORTED;
-  const WsLayout L = ws_layout(N, sp);
-  if (ws == nullptr || ws_bytes < L.total || ((uintptr_t)ws) % 256 != 0) return CE_ERR_WORKSPACE;
-  Args a = base_args(logits, ld, labels, N, V, ignore_index, ws);
-  a.slots = (uint64_t*)((char*)ws + L.slots);
-  a.grad = (char*)grad;
-  a.grad_ld = grad_ld;
-  a.dloss = dloss;
-  a.loss_mean = loss_mean;
-  a.loss_rows = loss_rows;
-  a.n_valid_out = n_valid;
-  a.status = status;
-  set_counters(a, counters_for(N, N));
-  const Cfg c = pick_cfg((V + 3) / 4);
-  KernelFn fn = (out_dtype == CE_DTYPE_BF16) ? f32to16_fn<cek::BF16>(c) : f32to16_fn<cek::F16>(c);
-  return launch(fn, N, c.nt, a, st);
 }
 
 int ce_abi_version(void) { return CE_ABI_VERSION; }

@@ -972,137 +972,6 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
 }
 
 // ---------------------------------------------------------------------------
-// fp32 logits in, 16-bit gradient out (the LM-head path: the logits of a chunk
-// come from an fp32-accumulated GEMM and the gradient feeds bf16 / fp16
-// GEMMs).  fp32 arithmetic throughout; one workgroup per row, the row in
-// VGPRs (NT x VPL vectors of 4 floats); the gradient is written to a separate
-// buffer of format TO (row i at grad + i * grad_ld elements), 8 bytes per
-// vector.  vocab is a multiple of 4, logits rows are 16-byte aligned and
-// gradient rows 8-byte aligned (the caller checks).
-// ---------------------------------------------------------------------------
-template <typename TO, int NT, int VPL, int MODE>
-__device__ __forceinline__ void pass2_f32(const u32x4 (&v)[VPL], int nvec, int tid, typename TO::bits_t* grow,
-                                          const GradConsts& kc, int kx, int ex) {
-#pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int idx = k * NT + tid;
-    if (idx < nvec) {
-      float g[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) g[d] = gelem<MODE>(as<float>(v[k][d]), kc);
-      if (k == kx) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) g[d] = (d == ex) ? kc.gy : g[d];
-      }
-      *(uint2*)(grow + (int64_t)idx * 4) = make_uint2(TO::pack(g[0], g[1]), TO::pack(g[2], g[3]));
-    }
-  }
-}
-
-template <typename TO, int NT, int VPL, int POL>
-__global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_f32_to16_kernel(Args a) {
-  constexpr int NW = NT / 64;
-  typedef typename TO::bits_t B;
-  __shared__ float lds_m[NW], lds_s[NW], lds_mn[NW];
-  __shared__ uint32_t lds_u[2 * NW + 4];
-  __shared__ double lds_d[NT];
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const uint32_t epoch = ld_agent(&a.ws->epoch);
-  const uint32_t tag = epoch + 1u;
-  if (row < a.K) count_and_publish<NT>(a, (int)row, tag, lds_u + 4);
-
-  const float* xrow = (const float*)(a.logits + row * a.ld * 4);
-  B* grow = (B*)a.grad + row * a.grad_ld;
-  const int64_t y = a.labels[row];
-  const bool ignored = (y == a.ignore);
-  const bool badlab = !ignored && (y < 0 || y >= a.V);
-  const int nvec = (int)(a.V >> 2);
-
-  u32x4 v[VPL];
-  if (!ignored) load_body<NT, VPL, POL>(v, Prefetch{(const u32x4*)xrow, nvec}, tid);
-  const float xy = (!ignored && !badlab) ? xrow[y] : 0.0f;
-  poll_to_lds(a, tag, lds_u);
-
-  float lse = 0.0f, loss = 0.0f, pcomp = 0.0f;
-  if (!ignored) {
-    float m = -INFINITY, mn = INFINITY;
-#pragma unroll
-    for (int k = 0; k < VPL; ++k)
-      if (k * NT + tid < nvec)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float x = as<float>(v[k][d]);
-          m = fmaxf(m, x);
-          mn = fminf(mn, x);
-        }
-    // the label's term is left out of the sum in the lane that holds it
-    int kx = -1, ex = 0;
-    if (!badlab) {
-      const int vy = (int)(y >> 2);
-      if (tid == vy % NT) {
-        kx = vy / NT;
-        ex = (int)(y & 3);
-      }
-    }
-    const float mc = (m == -INFINITY) ? 0.0f : m * kLog2e;
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPL; ++k)
-      if (k * NT + tid < nvec)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(as<float>(v[k][d]), kLog2e, -mc));
-          s += (k == kx && d == ex) ? 0.0f : e;
-        }
-    float M, S_ex, MN;
-    row_stats<NW>(m, s, mn, lds_m, lds_s, lds_mn, M, S_ex, MN);
-    if (badlab) {
-      lse = loss = pcomp = __builtin_nanf("");
-      const B q = (B)0x7fc0u;
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int idx = k * NT + tid;
-        if (idx < nvec) {
-          const uint32_t w = (uint32_t)q | ((uint32_t)q << 16);
-          *(uint2*)(grow + (int64_t)idx * 4) = make_uint2(w, w);
-        }
-      }
-    } else {
-      const float ey = __builtin_amdgcn_exp2f((xy - M) * kLog2e);
-      const float S = S_ex + ey;
-      lse = M + logf(S);
-      pcomp = S_ex / S;
-      loss = (pcomp >= 0.5f) ? (lse - xy) : log1pf(S_ex / ey);
-      const double scale_d = call_scale(a, lds_u);
-      const float scale = (float)scale_d;
-      const GradConsts kc = grad_consts<TO>(lse, scale, scale_d, (double)pcomp);
-      const float tmin = (MN - lse) * kLog2e;
-      const int mode = grad_mode<TO>(scale, tmin);
-      if (mode == kFold) pass2_f32<TO, NT, VPL, kFold>(v, nvec, tid, grow, kc, kx, ex);
-      else if (mode == kScaled) pass2_f32<TO, NT, VPL, kScaled>(v, nvec, tid, grow, kc, kx, ex);
-      else pass2_f32<TO, NT, VPL, kMul>(v, nvec, tid, grow, kc, kx, ex);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const int idx = k * NT + tid;
-      if (idx < nvec) *(uint2*)(grow + (int64_t)idx * 4) = make_uint2(0u, 0u);
-    }
-  }
-  if (tid == 0) {
-    a.loss_rows[row] = loss;
-    if (a.lse_rows) a.lse_rows[row] = (double)lse;
-    if (a.pcomp_rows) a.pcomp_rows[row] = (double)pcomp;
-    publish_loss(a, row, loss, tag);
-  }
-  if (blockIdx.x == gridDim.x - 1) {
-    __syncthreads();
-    finish_call<NT>(a, epoch, lds_u, lds_d);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Fused kernel for 16-byte-aligned 16-bit rows (vocab a multiple of 8 and a
 // 16-byte row stride), persistent, with buffer loads and stores.
 //

@@ -39,7 +39,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "ce_internal.h"
 #include "ce_mi355x.h"
 #include "lin_gemm.h"
 
