@@ -583,13 +583,25 @@ __device__ void finish_call(const Args& a, uint32_t epoch, const uint32_t* lds_u
 // ---------------------------------------------------------------------------
 // Lane passes over the staged vectors (16-bit formats, fp32 arithmetic).
 // ---------------------------------------------------------------------------
-// pass 0: lane max; for bf16 also a lower bound of the lane min.  The bf16
-// high element is read as the whole dword (its low half becomes extra
-// mantissa bits), which moves it by less than one bf16 ulp -- harmless for a
-// max used only as the stabilising shift.
+// pass 0: lane max; for bf16 also the lane min.  Both bf16 elements of a
+// dword are widened exactly (reading the high one as the whole dword would
+// turn a -inf next to a nonzero low half into a signalling NaN, which the
+// three-input max does not skip).
 // K0..K1: the vector slots taken (all by default; a vocabulary chunk of the
-// row otherwise).
-template <typename T, int NT, int VPL, int K0 = 0, int K1 = VPL>
+// row otherwise).  MIN = false leaves mn alone (callers that need no min).
+// The bf16 max and min take one three-input instruction per dword (the
+// compiler left most of them as two two-input ones).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <typename T, int NT, int VPL, int K0 = 0, int K1 = VPL, bool MIN = true>
 __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int tid, float& m, float& mn) {
 #pragma unroll
   for (int k = K0; k < K1; ++k) {
@@ -598,9 +610,9 @@ __device__ __forceinline__ void pass0_16(const u32x4 (&v)[VPL], int nvec, int ti
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint32_t u = v[k][d];
-          const float a0 = __builtin_bit_cast(float, u), a1 = __builtin_bit_cast(float, u << 16);
-          m = fmaxf(m, fmaxf(a0, a1));
-          mn = fminf(mn, fminf(a0, a1));
+          const float a0 = T::hi(u), a1 = T::lo(u);
+          m = max3f(m, a0, a1);
+          if constexpr (MIN) mn = min3f(mn, a0, a1);
         }
       } else {
         h2 hm = as<h2>(v[k][0]);
@@ -876,6 +888,7 @@ __device__ __forceinline__ void zero_row(char* gbase, const Geom& g, int tid, in
 // 256 VGPRs for a 512-lane shape and fit one row per CU.
 template <int NT, int VPL>
 constexpr int row_min_waves() { return (NT >= 512 && VPL <= 8) ? 8 : 4; }
+
 // The statistics pass holds no gradient state: 64 VGPRs for up to 8 vectors
 // per lane.  (With a 128-VGPR budget the scheduler has been seen to build up
 // more than 128 live values in the 256 x 8 shape and spill.)
@@ -920,7 +933,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
     float mn = INFINITY;
     if (has_h) mn = xh;
     if (has_t) mn = fminf(mn, xt);
-    pass0_16<T, NT, VPL>(v, g.nvec, tid, m, mn);
+    pass0_16<T, NT, VPL, 0, VPL, FUSED>(v, g.nvec, tid, m, mn);  // the min serves only the gradient
     const Owner own = owner<NT, EPV>(g, badlab ? -1 : y, tid);
     // the label element is left out of the sum: -inf in the registers of the
     // lane that holds it (kill_label), or in the head / tail element
@@ -947,8 +960,8 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
         const double scale_d = call_scale(a, lds_u);
         const float scale = (float)scale_d;
         const GradConsts kc = grad_consts<T>(lse, scale, scale_d, (double)pcomp);
-        // lower bound of (x - lse) log2e over the row (bf16 lane minima are
-        // lower bounds within one bf16 ulp; widen by 2^-7 relative)
+        // lower bound of (x - lse) log2e over the row (the lane minima are
+        // exact; the 2^-7 relative widening is a margin)
         const float tmin = (MN - fabsf(MN) * 0x1p-7f - lse) * kLog2e;
         const int64_t jt = g.head + (int64_t)g.nvec * EPV + tid;
         grad_row_16<T, NT, VPL, POL>(v, g.nvec, tid, (u32x4*)(gbase + g.head * ESZ), grad_mode<T>(scale, tmin), kc,
