@@ -20,11 +20,13 @@ Profiling (rocprofv3 databases -> profiles/ summaries):
     rocprofv3 --pmc FETCH_SIZE -d D -o fetch -- python bench.py --steps 5 --no-cpu-baseline --calibrate
     rocprofv3 --pmc WRITE_SIZE -d D -o write -- python bench.py --steps 5 --no-cpu-baseline --calibrate
     python bench.py --profile-summary D
-Every run also times a plain copy of the logits' size with the kernels' 16-byte
-nontemporal loads and stores under the same protocol (roofline.copy_ceiling,
-the attainable read + write rate); under the --calibrate runs the counters'
-reading of that copy gives the factor that turns FETCH_SIZE / WRITE_SIZE into
-bytes.
+Every run also times plain copies of the logits' size under the same protocol,
+in several shapes (cross_entropy_loss_amd/csrc/calib_copy.hip), and reports the
+fastest as roofline.copy_ceiling (the attainable read + write rate, with the
+shape in copy_shape); the split forward also gets the fastest plain read
+(read_ceiling).  Under the --calibrate runs only the first copy shape runs,
+and the counters' reading of it gives the factor that turns FETCH_SIZE /
+WRITE_SIZE into bytes.
 """
 from __future__ import annotations
 
@@ -466,26 +468,62 @@ def profile_summary_rope(d: str, workload: int) -> None:
                rw.T * rw.Hq * rw.D * rw.elem_bytes, sha)
 
 
-def _calib_copy_gbs(src, dst, nbytes, flush, stream, reps):
-    """Read + write rate of a plain copy of nbytes with the kernels' 16-byte
-    nontemporal loads and stores (median of the warm repetitions)."""
+COPY_SHAPES = ["grid-stride 16384 workgroups", "1 vector/thread", "4 vectors/thread", "8 vectors/thread",
+               "4 vectors/thread, cached", "persistent 8/CU, 4 vectors/thread"]
+
+
+def _calib_lib():
+    import ctypes
+    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
+    calib.ce_calib_copy_shape.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p]
+    calib.ce_calib_read_shape.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    return calib
+
+
+def _best_shape(launch, nbytes_moved, flush, stream, reps, shapes):
+    """Median time of each shape over `reps` flushed runs (the first dropped);
+    returns (best GB/s, shape index, {shape: GB/s})."""
+    import torch
+    rates = {}
+    for sh in shapes:
+        cms = []
+        for i in range(reps):
+            flush.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = launch(sh)
+            e1.record(stream)
+            if rc:
+                raise SystemExit(f"calibration kernel (shape {sh}) failed: {rc}")
+            torch.cuda.synchronize()
+            cms.append(e0.elapsed_time(e1))
+        rates[sh] = nbytes_moved / (float(np.median(cms[1:])) * 1e-3) / 1e9
+    best = max(rates, key=rates.get)
+    return rates[best], best, rates
+
+
+def _calib_copy(src, dst, nbytes, flush, stream, calibrate):
+    """The attainable read + write rate for nbytes: the fastest copy shape
+    (only shape 0, the counters' calibration copy, under --calibrate)."""
+    import ctypes
+    calib = _calib_lib()
+    shapes = [0] if calibrate else list(range(calib.ce_calib_shapes()))
+    launch = lambda sh: calib.ce_calib_copy_shape(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                                  nbytes, sh, ctypes.c_void_p(stream.cuda_stream))
+    return _best_shape(launch, 2 * nbytes, flush, stream, 3 if calibrate else 5, shapes)
+
+
+def _calib_read(src, nbytes, flush, stream):
+    """The attainable read rate for nbytes: the fastest read shape."""
     import ctypes
     import torch
-    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
-    calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-    cms = []
-    for i in range(reps):
-        flush.fill_(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        rc = calib.ce_calib_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
-                                 ctypes.c_void_p(stream.cuda_stream))
-        e1.record(stream)
-        if rc:
-            raise SystemExit(f"calibration copy failed: {rc}")
-        torch.cuda.synchronize()
-        cms.append(e0.elapsed_time(e1))
-    return 2 * nbytes / (float(np.median(cms[1:])) * 1e-3) / 1e9
+    calib = _calib_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device=src.device)
+    launch = lambda sh: calib.ce_calib_read_shape(ctypes.c_void_p(src.data_ptr()), nbytes, sh,
+                                                  ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+    return _best_shape(launch, nbytes, flush, stream, 5, list(range(calib.ce_calib_shapes())))
 
 
 def bench_rmsnorm(args) -> None:
@@ -535,8 +573,8 @@ def bench_rmsnorm(args) -> None:
     wall = time.perf_counter() - t0
     fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    copy_gbs = _calib_copy_gbs(xd, torch.empty_like(xd), nw.N * nw.H * nw.elem_bytes, flush, stream,
-                               3 if args.calibrate else 7)
+    copy_gbs, copy_shape, _ = _calib_copy(xd, torch.empty_like(xd), nw.N * nw.H * nw.elem_bytes, flush, stream,
+                                          args.calibrate)
     ab = norm_bytes(nw)
     step_ms = float(fwd.mean() + bwd.mean())
     bw_gbs = ab["backward"] / (float(bwd.mean()) * 1e-3) / 1e9
@@ -556,7 +594,7 @@ def bench_rmsnorm(args) -> None:
         "config": {"workload": nw.name, "rows": nw.N, "hidden": nw.H, "eps": nw.eps, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "backward call: rms_bwd16 + rms_dw_reduce", "achieved": bw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": bw_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "copy_ceiling": copy_gbs, "frac_of_copy": bw_gbs / copy_gbs},
+                     "copy_ceiling": copy_gbs, "frac_of_copy": bw_gbs / copy_gbs, "copy_shape": COPY_SHAPES[copy_shape]},
         "timing": {"forward_ms_mean": float(fwd.mean()), "forward_ms_median": float(np.median(fwd)),
                    "forward_gbs": fw_gbs, "backward_ms_mean": float(bwd.mean()),
                    "backward_ms_median": float(np.median(bwd)), "algorithmic_bytes": ab,
@@ -621,8 +659,8 @@ def bench_rope(args) -> None:
     wall = time.perf_counter() - t0
     fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    copy_gbs = _calib_copy_gbs(qd, torch.empty_like(qd), qd.numel() * qd.element_size(), flush, stream,
-                               3 if args.calibrate else 7)
+    copy_gbs, copy_shape, _ = _calib_copy(qd, torch.empty_like(qd), qd.numel() * qd.element_size(), flush, stream,
+                                          args.calibrate)
     ab = rope_bytes(rw)
     step_ms = float(fwd.mean() + bwd.mean())
     per_launch_ms = step_ms / 2
@@ -644,7 +682,7 @@ def bench_rope(args) -> None:
                    "base": rw.base, "sequences": int((pos == 0).sum()), "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "rope16 (one launch: q and k)", "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "copy_ceiling": copy_gbs,
-                     "frac_of_copy": gbs / copy_gbs},
+                     "frac_of_copy": gbs / copy_gbs, "copy_shape": COPY_SHAPES[copy_shape]},
         "timing": {"forward_ms_mean": float(fwd.mean()), "forward_ms_median": float(np.median(fwd)),
                    "inverse_ms_mean": float(bwd.mean()), "inverse_ms_median": float(np.median(bwd)),
                    "algorithmic_bytes_per_launch": ab, "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
@@ -743,7 +781,9 @@ def bench_split(args) -> None:
     fms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     nbytes = pristine.numel() * pristine.element_size()
-    copy_gbs = _calib_copy_gbs(pristine, work, nbytes, flush, stream, 3 if args.calibrate else 7)
+    copy_gbs, copy_shape, _ = _calib_copy(pristine, work, nbytes, flush, stream, args.calibrate)
+    # the forward only reads the logits: its ceiling is the fastest plain read
+    read_gbs, read_shape, _ = _calib_read(pristine, nbytes, flush, stream)
     b = split_bytes(w, labels)
     traffic = None
     cpath = os.path.join(ROOT, "profiles", f"ce_split_{w.name}.counters.json")
@@ -755,8 +795,13 @@ def bench_split(args) -> None:
 
     def roof(part, ms_mean):
         a = b[part] / (ms_mean * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS,
-                "traffic": traffic[part] if traffic else None, "copy_ceiling": copy_gbs, "frac_of_copy": a / copy_gbs}
+        r = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS,
+             "traffic": traffic[part] if traffic else None}
+        if part == "forward":
+            r.update({"read_ceiling": read_gbs, "frac_of_read": a / read_gbs, "read_shape": COPY_SHAPES[read_shape]})
+        else:
+            r.update({"copy_ceiling": copy_gbs, "frac_of_copy": a / copy_gbs, "copy_shape": COPY_SHAPES[copy_shape]})
+        return r
 
     f_mean, b_mean = float(fms.mean()), float(bms.mean())
     rec = {
@@ -862,26 +907,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
-    # the measured ceiling: a plain copy of the logits' size (the same 16-byte
-    # nontemporal loads and stores) under the same protocol; with --calibrate
-    # its counter readings also scale FETCH_SIZE / WRITE_SIZE
-    import ctypes
-    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
-    calib.ce_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    # the measured ceiling: the fastest plain copy of the logits' size under
+    # the same protocol; with --calibrate only the counters' calibration copy
+    # runs, and its counter readings scale FETCH_SIZE / WRITE_SIZE
     nbytes = pristine.numel() * pristine.element_size()
-    cms = []
-    for i in range(3 if args.calibrate else 7):
-        flush.fill_(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        rc = calib.ce_calib_copy(ctypes.c_void_p(pristine.data_ptr()), ctypes.c_void_p(work.data_ptr()), nbytes,
-                                 ctypes.c_void_p(stream.cuda_stream))
-        e1.record(stream)
-        if rc:
-            raise SystemExit(f"calibration copy failed: {rc}")
-        torch.cuda.synchronize()
-        cms.append(e0.elapsed_time(e1))
-    copy_gbs = 2 * nbytes / (float(np.median(cms[1:])) * 1e-3) / 1e9
+    copy_gbs, copy_shape, copy_rates = _calib_copy(pristine, work, nbytes, flush, stream, args.calibrate)
     st = int(out["status"].item())
     if st != 0:
         raise SystemExit(f"kernel status {st:#x}")
@@ -908,7 +938,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "counter_gbs": traffic / (ms_mean * 1e-3) / 1e9 if traffic else None,
-                     "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+                     "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs,
+                     "copy_shape": COPY_SHAPES[copy_shape],
+                     "copy_shapes_gbs": {COPY_SHAPES[k]: round(v, 1) for k, v in copy_rates.items()}},
         "timing": {"ms_p10": float(np.percentile(ms, 10)), "ms_median": float(np.median(ms)),
                    "ms_p90": float(np.percentile(ms, 90)), "algorithmic_bytes": abytes,
                    "valid_tokens_per_s": n_valid / (ms_mean * 1e-3),

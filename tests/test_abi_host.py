@@ -325,3 +325,23 @@ def test_rope_empty_calls_are_no_ops(lib):
 ])
 def test_rope_rejects(lib, kw, code):
     assert rope_call(lib, **kw) == code
+
+
+def test_calibration_copy_library_rejects():
+    """The benchmark's plain-copy library: every shape is addressable and bad
+    arguments are refused before any launch."""
+    calib = ctypes.CDLL(os.path.join(ROOT, "cross_entropy_loss_amd", "libce_calib.so"))
+    calib.ce_calib_copy_shape.argtypes = [VP, VP, ctypes.c_size_t, ctypes.c_int, VP]
+    calib.ce_calib_read_shape.argtypes = [VP, ctypes.c_size_t, ctypes.c_int, VP, VP]
+    calib.ce_calib_copy.argtypes = [VP, VP, ctypes.c_size_t, VP]
+    n = calib.ce_calib_shapes()
+    assert n >= 2
+    for sh in (-1, n):
+        assert calib.ce_calib_copy_shape(VP(FAKE), VP(FAKE), 1024, sh, None) == 1
+        assert calib.ce_calib_read_shape(VP(FAKE), 1024, sh, VP(FAKE), None) == 1
+    assert calib.ce_calib_copy_shape(VP(FAKE), VP(FAKE), 1000, 0, None) == 1      # not a multiple of 16
+    assert calib.ce_calib_copy_shape(VP(FAKE + 8), VP(FAKE), 1024, 0, None) == 1  # misaligned
+    assert calib.ce_calib_copy_shape(None, VP(FAKE), 1024, 0, None) == 1
+    assert calib.ce_calib_read_shape(VP(FAKE), 1024, 0, None, None) == 1          # no sink
+    assert calib.ce_calib_copy(VP(FAKE), VP(FAKE), 1000, None) == 1
+    assert calib.ce_calib_copy_shape(VP(FAKE), VP(FAKE), 0, 3, None) == 0         # empty: nothing launched
