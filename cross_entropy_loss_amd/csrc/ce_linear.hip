@@ -136,14 +136,26 @@ __device__ __forceinline__ float get_tagged(const uint64_t* p, uint32_t tag, uin
   }
 }
 
-__device__ __forceinline__ float half_max(float v) {
+// A tagged word's load, and its value once loaded (polled for when the word
+// is not yet this call's): a thread issues all its loads before it checks
+// any, so the exchange costs one round trip rather than one per word.
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tagged_value(uint64_t w, const uint64_t* p, uint32_t tag, uint32_t& to) {
+  if ((uint32_t)(w >> 32) == tag) return __builtin_bit_cast(float, (uint32_t)w);
+  return get_tagged(p, tag, to);
+}
+
+// Whole-wave max / sum (every lane gets the result; fixed order).
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ float half_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
@@ -243,13 +255,22 @@ struct LogitsArgs {
 // quarters (136 KB) at offset 16 KB: all of a CU's 160 KB.
 constexpr int kLogitsLds = 160 * 1024;
 static_assert(16384 + 4 * 128 * 136 * 2 <= kLogitsLds, "staged gradient quarters");
-static_assert(16384 + 256 * 72 * 4 <= kLogitsLds, "statistics transpose");
+static_assert(16384 + 256 * 65 * 4 <= kLogitsLds, "statistics transpose");
+
+// Row of accumulator element v of 32-row block i within a lane's rows (the
+// lane's first row is wm * 128 + 4 * (lane / 32); see lg::acc_row).
+__device__ constexpr int kRowOff(int i, int v) { return i * 32 + 8 * (v >> 2) + (v & 3); }
+// Tiles per lane and round of the row merge (128 tiles a round).
+constexpr int kMergeQ = 2;
 
 template <typename T, bool DMA, int AK, int BKD>
 __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int rt = (int)(blockIdx.x % a.rtc), vt = (int)(blockIdx.x / a.rtc);
+  // the row tiles that share a weight slab are neighbours in the XCD order,
+  // so they run on one XCD and the slab is fetched into its L2 once
+  const int lin = lg::xcd_order((int)blockIdx.x, a.rtc * a.nvt);
+  const int rt = lin % a.rtc, vt = lin / a.rtc;
   const int64_t mrow0 = a.row0 + (int64_t)rt * 256;  // the tile's first row (global)
   const int n0 = vt * 256;
   const int M = (int)a.N, Nv = (int)a.V, K = (int)a.H;
@@ -261,16 +282,16 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   __syncthreads();  // every wave is done with the K loop's LDS
 
   // LDS after the K loop: per-row label data and statistics, and a
-  // [256][kPS] transpose area for the per-lane partials (kPS = 72 floats per
-  // row puts the two half-waves, four rows apart, on disjoint banks).  The
+  // [256][kPS] transpose area for the per-lane partials (kPS = 65 floats per
+  // row: the row reductions, one thread per row, read without bank
+  // conflicts; the half-waves' writes, four rows apart, overlap on 28 banks).  The
   // epilogue walks the accumulators one 32-row block (index i) at a time so
   // that only that block's row constants are held in registers.
-  constexpr int kPS = 72;
+  constexpr int kPS = 65;
   int64_t* ys = (int64_t*)lds;              // [256] labels of the tile's rows
   int32_t* yrel = (int32_t*)(lds + 2048);   // [256] label column - n0 when in this tile, else -1
   float* mrow = (float*)(lds + 3072);       // [256] the tile's row max
   float* xyl = (float*)(lds + 4096);        // [256 + 64] label logits found here (+ junk slots)
-  float* pm = (float*)(lds + 6144);         // merge inputs: [<= 512][2]
   float* lrow = (float*)(lds + 10240);      // [256] lse of the tile's rows
   float* prow = (float*)(lds + 11264);      // [256] 1 - p_y
   uint32_t* sflag = (uint32_t*)(lds + 12288);
@@ -287,21 +308,33 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   bool cvalid[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) cvalid[j] = n0 + lc + 32 * j < Nv;
+  // every column of the tile inside the vocabulary (all tiles but the last):
+  // the passes below then take no per-element column test
+  const bool full = n0 + 256 <= Nv;
+  // this lane's slot of row acc_row(wm, i, v, lane) in the transpose area:
+  // part_l[kRowOff(i, v) * kPS], a compile-time offset per (i, v)
+  float* part_l = part + (wm * 128 + 4 * (lane >> 5)) * kPS + wn * 32 + (lane & 31);
   // pass A: per lane and row the max over its four columns, through LDS to
   // one thread per row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float m[16];
+    if (full) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) m[v] = -INFINITY;
+      for (int v = 0; v < 16; ++v)
+        m[v] = fmaxf(fmaxf(t.acc[i][0][v], t.acc[i][1][v]), fmaxf(t.acc[i][2][v], t.acc[i][3][v]));
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16 blk = t.acc[i][j];
+      for (int v = 0; v < 16; ++v) m[v] = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) m[v] = fmaxf(m[v], cvalid[j] ? blk[v] : -INFINITY);
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 blk = t.acc[i][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m[v] = fmaxf(m[v], cvalid[j] ? blk[v] : -INFINITY);
+      }
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) part[lg::acc_row(wm, i, v, lane) * kPS + wn * 32 + (lane & 31)] = m[v];
+    for (int v = 0; v < 16; ++v) part_l[kRowOff(i, v) * kPS] = m[v];
   }
   __syncthreads();
   {
@@ -313,11 +346,14 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   }
   __syncthreads();
   // pass B: the label-excluded sums relative to the row max; the lane that
-  // holds a row's label logit leaves it in xyl (others write a junk slot)
+  // holds a row's label logit leaves it in xyl (others write a junk slot).
+  // A wave whose 32-row block holds no label of its columns (most blocks)
+  // sums without per-element tests.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float mc[16], sv[16], xv[16];
     int lj[16];
+    bool lab = false;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = lg::acc_row(wm, i, v, lane);
@@ -325,24 +361,36 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
       mc[v] = (mr == -INFINITY) ? 0.0f : mr * kLog2e;
       const int d = yrel[r] - lc;  // the label's column is this lane's in block d / 32
       lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
+      lab = lab || lj[v] >= 0;
       sv[v] = 0.0f;
       xv[v] = 0.0f;
     }
+    if (full && __ballot(lab) == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16 blk = t.acc[i][j];
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 blk = t.acc[i][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sv[v] += __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part_l[kRowOff(i, v) * kPS] = sv[v];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 blk = t.acc[i][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
+          sv[v] += (cvalid[j] && lj[v] != j) ? e : 0.0f;
+          xv[v] = (lj[v] == j) ? blk[v] : xv[v];
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
-        sv[v] += (cvalid[j] && lj[v] != j) ? e : 0.0f;
-        xv[v] = (lj[v] == j) ? blk[v] : xv[v];
+        const int r = lg::acc_row(wm, i, v, lane);
+        part_l[kRowOff(i, v) * kPS] = sv[v];
+        xyl[(lj[v] >= 0) ? r : 256 + lane] = xv[v];
       }
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = lg::acc_row(wm, i, v, lane);
-      part[r * kPS + wn * 32 + (lane & 31)] = sv[v];
-      xyl[(lj[v] >= 0) ? r : 256 + lane] = xv[v];
     }
   }
   __syncthreads();
@@ -360,44 +408,61 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
     }
   }
 
-  // rows r = vt, vt + nvt, ... of this row tile are merged here
+  // rows r = vt, vt + nvt, ... of this row tile are merged here, one wave per
+  // row: its lanes fetch the nvt tiles' (max, sum) words (all loads issued
+  // before any is waited on), merge their own, and the wave merges the lanes
   uint32_t to = 0;
-  int nA = 0;
-  for (int r = vt; r < 256 && mrow0 + r < a.N; r += a.nvt) ++nA;
-  for (int p = tid; p < nA * a.nvt; p += 256) {
-    const int k = p / a.nvt, v2 = p % a.nvt, r = vt + k * a.nvt;
-    const int64_t y = ys[r];
-    if (y == a.ignore || y < 0 || y >= a.V) continue;
-    const uint64_t* sp = a.stats + ((size_t)(rt * 256 + r) * a.nvt + v2) * 2;
-    pm[p * 2] = get_tagged(sp, tag, to);
-    pm[p * 2 + 1] = get_tagged(sp + 1, tag, to);
-  }
-  __syncthreads();
-  if (tid < nA) {
-    const int r = vt + tid * a.nvt;
+  for (int k = wave;; k += 4) {
+    const int r = vt + k * a.nvt;
+    if (r >= 256 || mrow0 + r >= a.N) break;
     const int64_t R = mrow0 + r, y = ys[r];
     float loss = 0.0f;
     if (y != a.ignore) {
       if (y < 0 || y >= a.V) {
         loss = __builtin_nanf("");
       } else {
-        float Mx = -INFINITY;
-        for (int v2 = 0; v2 < a.nvt; ++v2) Mx = fmaxf(Mx, pm[(tid * a.nvt + v2) * 2]);
-        float S = 0.0f;
-        for (int v2 = 0; v2 < a.nvt; ++v2) {
-          const float mv = pm[(tid * a.nvt + v2) * 2], sv = pm[(tid * a.nvt + v2) * 2 + 1];
-          if (mv != -INFINITY) S += sv * __builtin_amdgcn_exp2f((mv - Mx) * kLog2e);
+        const uint64_t* sp = a.stats + (size_t)(rt * 256 + r) * a.nvt * 2;
+        const uint64_t wxy = ld_tagged(a.xy + R);
+        float ml = -INFINITY, sl = 0.0f;  // this lane's running (max, sum)
+        for (int v0 = 0; v0 < a.nvt; v0 += 64 * kMergeQ) {
+          uint64_t wm_[kMergeQ], ws_[kMergeQ];
+#pragma unroll
+          for (int q = 0; q < kMergeQ; ++q) {
+            const int v2 = v0 + lane + 64 * q;
+            if (v2 < a.nvt) {
+              wm_[q] = ld_tagged(sp + v2 * 2);
+              ws_[q] = ld_tagged(sp + v2 * 2 + 1);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kMergeQ; ++q) {
+            const int v2 = v0 + lane + 64 * q;
+            if (v2 < a.nvt) {
+              const float mv = tagged_value(wm_[q], sp + v2 * 2, tag, to);
+              const float sv = tagged_value(ws_[q], sp + v2 * 2 + 1, tag, to);
+              if (mv != -INFINITY) {
+                const float mn = fmaxf(ml, mv);
+                sl = ((ml == -INFINITY) ? 0.0f : sl * __builtin_amdgcn_exp2f((ml - mn) * kLog2e)) +
+                     sv * __builtin_amdgcn_exp2f((mv - mn) * kLog2e);
+                ml = mn;
+              }
+            }
+          }
         }
-        const float xy = get_tagged(a.xy + R, tag, to);
+        const float Mx = wave_max(ml);
+        const float S = wave_sum((ml == -INFINITY) ? 0.0f : sl * __builtin_amdgcn_exp2f((ml - Mx) * kLog2e));
+        const float xy = tagged_value(wxy, a.xy + R, tag, to);
         const float ey = __builtin_amdgcn_exp2f((xy - Mx) * kLog2e);
         const float St = S + ey;
         const float l = Mx + logf(St), pcomp = S / St;
         loss = (pcomp >= 0.5f) ? (l - xy) : log1pf(S / ey);
-        put_tagged(a.lse + R, tag, l);
-        put_tagged(a.pc + R, tag, pcomp);
+        if (lane == 0) {
+          put_tagged(a.lse + R, tag, l);
+          put_tagged(a.pc + R, tag, pcomp);
+        }
       }
     }
-    a.loss_rows[R] = loss;
+    if (lane == 0) a.loss_rows[R] = loss;
   }
   // every row of the tile: its lse and 1 - p_y
   {
@@ -405,8 +470,9 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
     const int64_t R = mrow0 + r, y = ys[r];
     float l = 0.0f, pcv = 0.0f;
     if (R < a.N && y != a.ignore && y >= 0 && y < a.V) {
-      l = get_tagged(a.lse + R, tag, to);
-      pcv = get_tagged(a.pc + R, tag, to);
+      const uint64_t wl = ld_tagged(a.lse + R), wp = ld_tagged(a.pc + R);
+      l = tagged_value(wl, a.lse + R, tag, to);
+      pcv = tagged_value(wp, a.pc + R, tag, to);
     }
     lrow[r] = l;
     prow[r] = pcv;
@@ -424,40 +490,89 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   constexpr int kGS = 136;  // staged row stride in elements
   __syncthreads();  // the statistics area is free
   uint16_t* stg = (uint16_t*)(lds + 16384 + wave * (128 * kGS * 2));
+  // The common case (a full tile, s > 0, every exchange in time) writes
+  // 2^(x log2 e - b) everywhere, then fixes up the few special elements:
+  // the label's, ignored rows (+0) and rows with a bad label (NaN).
+  const bool fast = full && gs > 0.0f && !bad_scale;
+  const int64_t cbase = (int64_t)n0 + wn * 128;
+  if (fast) {
+    uint16_t* stg_l = stg + 4 * (lane >> 5) * kGS + (lane & 31);  // + kRowOff(i, v) * kGS + 32 j
+    const uint32_t nanb = to_bits<T>(__builtin_nanf("")), nan2 = (nanb << 16) | nanb;
+    // 32 rows of the quarter at a time: computed, fixed up and stored, so the
+    // stores of one block overlap the arithmetic of the next
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float bv[16], gyv[16], mul[16];
-    int lj[16], kind[16];  // kind: 0 normal, 1 zero (ignored row), 2 NaN (bad label or failed exchange)
+    for (int i = 0; i < 4; ++i) {
+      float bv[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = lg::acc_row(wm, i, v, lane);
-      const int64_t y = ys[r];
-      const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
-      kind[v] = ign ? 1 : ((bad || bad_scale) ? 2 : 0);
-      // g = 2^(x log2 e - b) * mul: b folds log2 s in when s > 0
-      bv[v] = lrow[r] * kLog2e - (gs > 0.0f ? lgs : 0.0f);
-      mul[v] = (gs > 0.0f) ? 1.0f : gs;
-      gyv[v] = -gs * prow[r];
-      const int d = yrel[r] - lc;
-      lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
+      for (int v = 0; v < 16; ++v) bv[v] = lrow[lg::acc_row(wm, i, v, lane)] * kLog2e - lgs;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 blk = t.acc[i][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])));
+      }
+      // fix-ups of rows 32 i .. 32 i + 31, after this wave's own staged
+      // writes (LDS keeps a wave's order): the label's element, ignored rows
+      // (+0), rows with a bad label (NaN)
+      {
+        const int rq = i * 32 + (lane & 31), r = wm * 128 + rq;
+        const int64_t y = ys[r];
+        const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
+        const uint64_t zb = __ballot(lane < 32 && ign), nb = __ballot(lane < 32 && bad);
+        const int d = yrel[r] - wn * 128;  // the label's column in this quarter
+        if (lane < 32 && !ign && !bad && d >= 0 && d < 128) stg[rq * kGS + d] = to_bits<T>(-gs * prow[r]);
+        for (uint64_t b = zb; b; b &= b - 1) ((uint32_t*)(stg + (i * 32 + __builtin_ctzll(b)) * kGS))[lane] = 0u;
+        for (uint64_t b = nb; b; b &= b - 1) ((uint32_t*)(stg + (i * 32 + __builtin_ctzll(b)) * kGS))[lane] = nan2;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int rr = i * 32 + q * 4 + (lane >> 4), cv = (lane & 15) * 8;
+        const int64_t R = mrow0 + wm * 128 + rr;
+        const int64_t c = cbase + cv;
+        if (R < a.N && c < a.ldg) {
+          const lg::u32x4 val = *(const lg::u32x4*)(stg + rr * kGS + cv);
+          *(lg::u32x4*)(a.g + R * a.ldg + c) = val;
+        }
+      }
     }
+    return;
+  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16 blk = t.acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      float bv[16], gyv[16], mul[16];
+      int lj[16], kind[16];  // kind: 0 normal, 1 zero (ignored row), 2 NaN (bad label or failed exchange)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float gv = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])) * mul[v];
-        gv = (lj[v] == j) ? gyv[v] : gv;
-        gv = (kind[v] == 2) ? __builtin_nanf("") : gv;
-        gv = (kind[v] == 1 || !cvalid[j]) ? 0.0f : gv;
         const int r = lg::acc_row(wm, i, v, lane);
-        stg[(r - wm * 128) * kGS + (lc - wn * 128) + 32 * j] = to_bits<T>(gv);
+        const int64_t y = ys[r];
+        const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
+        kind[v] = ign ? 1 : ((bad || bad_scale) ? 2 : 0);
+        // g = 2^(x log2 e - b) * mul: b folds log2 s in when s > 0
+        bv[v] = lrow[r] * kLog2e - (gs > 0.0f ? lgs : 0.0f);
+        mul[v] = (gs > 0.0f) ? 1.0f : gs;
+        gyv[v] = -gs * prow[r];
+        const int d = yrel[r] - lc;
+        lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 blk = t.acc[i][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float gv = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])) * mul[v];
+          gv = (lj[v] == j) ? gyv[v] : gv;
+          gv = (kind[v] == 2) ? __builtin_nanf("") : gv;
+          gv = (kind[v] == 1 || !cvalid[j]) ? 0.0f : gv;
+          const int r = lg::acc_row(wm, i, v, lane);
+          stg[(r - wm * 128) * kGS + (lc - wn * 128) + 32 * j] = to_bits<T>(gv);
+        }
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
   // 128 rows x 16 vectors of the quarter: four rows per pass of the wave
-  const int64_t cbase = (int64_t)n0 + wn * 128;
 #pragma unroll 4
   for (int q = 0; q < 32; ++q) {
     const int rr = q * 4 + (lane >> 4), cv = (lane & 15) * 8;

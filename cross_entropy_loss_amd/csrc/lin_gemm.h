@@ -627,39 +627,33 @@ __device__ __forceinline__ void tile_rs(Tile& t, char* lds, const char* A, int64
     rs_step<T, AK, BKD>(t, lds, kt, KT, K, wm, wn, wave, lane, tid, la, lb, sa, sb, a0, b0, a1, b1);
 }
 
-// Tile order for a grid of mt x nt tiles: workgroups are placed on the 8
-// XCDs round-robin by id, so the id is split into (XCD, index on the XCD)
-// and each XCD walks whole columns of row tiles: the mt row tiles that share
-// one B tile (a slab of the weight) run on one XCD, close in time, and the
-// B tile is fetched into that XCD's L2 once.
-__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& m_tile, int& n_tile) {
-  const int total = mt * nt;
+// Workgroups are placed on the 8 XCDs round-robin by id.  xcd_order(bid,
+// total) renumbers a grid of `total` workgroups so that each XCD takes one
+// contiguous range of the new order (XCD x: the ids b = x mod 8, in
+// increasing order), whatever the grid size.
+__device__ __forceinline__ int xcd_order(int bid, int total) {
   const int x = bid & 7, q = bid >> 3;
-  const int per = total >> 3;  // ids per XCD when the grid is a multiple of 8
-  if ((total & 7) == 0) {
-    const int lin = x * per + q;  // this XCD's contiguous share of the column-major order
-    n_tile = lin / mt;
-    m_tile = lin % mt;
-  } else {
-    n_tile = bid / mt;
-    m_tile = bid % mt;
-  }
+  const int per = total >> 3, extra = total & 7;  // XCDs below `extra` take one more
+  return x * per + (x < extra ? x : extra) + q;
+}
+
+// Tile order for a grid of mt x nt tiles: each XCD walks whole columns of row
+// tiles, so the mt row tiles that share one B tile (a slab of the weight) run
+// on one XCD, close in time, and the B tile is fetched into that XCD's L2
+// once.
+__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& m_tile, int& n_tile) {
+  const int lin = xcd_order(bid, mt * nt);
+  n_tile = lin / mt;
+  m_tile = lin % mt;
 }
 
 // The same with each XCD walking whole rows of column tiles: the nt column
 // tiles that share one A tile run on one XCD (for products whose A operand
 // is the larger one).
 __device__ __forceinline__ void tile_of_rows(int bid, int mt, int nt, int& m_tile, int& n_tile) {
-  const int total = mt * nt;
-  const int x = bid & 7, q = bid >> 3;
-  if ((total & 7) == 0) {
-    const int lin = x * (total >> 3) + q;
-    m_tile = lin / nt;
-    n_tile = lin % nt;
-  } else {
-    m_tile = bid / nt;
-    n_tile = bid % nt;
-  }
+  const int lin = xcd_order(bid, mt * nt);
+  m_tile = lin / nt;
+  n_tile = lin % nt;
 }
 
 // Row and column of accumulator element v of block (i, j) in this lane,
