@@ -225,9 +225,9 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
 }
 
 // ---------------------------------------------------------------------------
-// 2. logits tile + cross-entropy epilogue (16-bit; cooperative launch per
-// chunk of row tiles).  Grid: rt_chunk x nvt workgroups; blockIdx.x = vt *
-// rtc + rt, so the row tiles that share a weight slab run side by side.
+// 2. logits tile + cross-entropy epilogue (16-bit; cooperative launches over
+// chunks of row tiles).  Grid: rt x nvt workgroups in the XCD order, so the
+// row tiles that share a weight slab run on one XCD.
 // ---------------------------------------------------------------------------
 struct LogitsArgs {
   const char* h;
@@ -240,10 +240,11 @@ struct LogitsArgs {
   int64_t row0;  // first row of this chunk
   int rtc;       // row tiles in this chunk
   int nvt;
+  int rt_chunk, nchunks, rt_total;  // row tiles per chunk, chunks, row tiles in all
   LinHeader* hdr;
   uint16_t* g;
   int64_t ldg;
-  uint64_t* stats;  // this chunk's [rtc * 256][nvt][2]
+  uint64_t* stats;  // this chunk's [rtc * 256][nvt][2] (every chunk's in the one-launch form)
   uint64_t* xy;     // [N]
   uint64_t* lse;    // [N]
   uint64_t* pc;     // [N]
@@ -264,18 +265,21 @@ __device__ constexpr int kRowOff(int i, int v) { return i * 32 + 8 * (v >> 2) + 
 constexpr int kMergeQ = 2;
 
 template <typename T, bool DMA, int AK, int BKD>
-__global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+// One tile of one chunk: workgroup blockIdx.x of a grid of rtg x nvt takes
+// tile (rt, vt) of the chunk (none when rt is past the chunk's rtc row tiles).
+// tid is the thread index (opaque to the compiler in the one-launch loop).
+__device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, int tid, int rtg) {
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
   // the row tiles that share a weight slab are neighbours in the XCD order,
   // so they run on one XCD and the slab is fetched into its L2 once
-  const int lin = lg::xcd_order((int)blockIdx.x, a.rtc * a.nvt);
-  const int rt = lin % a.rtc, vt = lin / a.rtc;
+  const int lin = lg::xcd_order((int)blockIdx.x, rtg * a.nvt);
+  const int rt = lin % rtg, vt = lin / rtg;
+  if (rt >= a.rtc) return;  // the last chunk may have fewer row tiles
   const int64_t mrow0 = a.row0 + (int64_t)rt * 256;  // the tile's first row (global)
   const int n0 = vt * 256;
   const int M = (int)a.N, Nv = (int)a.V, K = (int)a.H;
   Tile t;
-  if constexpr (DMA) lg::tile_nt<T>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
+  if constexpr (DMA) lg::tile_nt<T>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0, tid);
   else lg::tile_rs<T, AK, BKD>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
   const uint32_t tag = a.hdr->epoch;
   const float gs = a.hdr->gscale;
@@ -585,6 +589,35 @@ __global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
   }
 }
 
+// The direct-to-LDS form walks every chunk in one cooperative launch: each
+// workgroup takes tile (rt, vt) of chunk 0, 1, ... in turn.  The row tiles of
+// a chunk exchange their statistics through slots of their own and every
+// workgroup walks the chunks in the same order, so the waits of chunk c only
+// involve workgroups that reach chunk c.  (One cooperative launch per chunk
+// leaves the GPU idle ~19 us between chunks.)  The element-wise form, which
+// the compiler cannot keep free of spills in the loop, launches per chunk.
+template <typename T, bool DMA, int AK, int BKD>
+__global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if constexpr (DMA) {
+    uint64_t* stats0 = a.stats;
+    for (int c = 0; c < a.nchunks; ++c) {
+      LogitsArgs ac = a;
+      ac.row0 = (int64_t)c * a.rt_chunk * 256;
+      ac.rtc = min(a.rt_chunk, a.rt_total - c * a.rt_chunk);
+      ac.stats = stats0 + (size_t)c * a.rt_chunk * 256 * a.nvt * 2;
+      // a thread index the compiler cannot see through, so nothing
+      // lane-dependent is hoisted out of this loop and held across a tile
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      logits_ce_tile<T, DMA, AK, BKD>(ac, lds, tid, a.rt_chunk);
+      __syncthreads();  // the LDS is free for the next chunk's K loop
+    }
+  } else {
+    logits_ce_tile<T, DMA, AK, BKD>(a, lds, (int)threadIdx.x, a.rtc);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 3-4. dh = g W and dW = g^T h (16-bit): MFMA tiles, 2^-k on output.
 // ---------------------------------------------------------------------------
@@ -859,16 +892,29 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
   auto kfn = fast ? lin_logits_ce_kernel<T, true, lg::kKC, lg::kKC> : lin_logits_ce_kernel<T, false, lg::kKCg, lg::kKCg>;
   const int lds_bytes = kLogitsLds;
   if (set_lds(kfn, lds_bytes) != CE_OK) return CE_ERR_HIP;
-  for (int c = 0; c < L.nchunks; ++c) {
-    const int64_t rt0 = (int64_t)c * L.rt_chunk;
-    const int rtc = (int)((rt_total - rt0 < L.rt_chunk) ? rt_total - rt0 : L.rt_chunk);
-    la.row0 = rt0 * 256;
-    la.rtc = rtc;
-    la.stats = (uint64_t*)(ws + L.stats) + (size_t)c * L.rt_chunk * 256 * L.nvt * 2;
+  la.rt_chunk = L.rt_chunk;
+  la.nchunks = L.nchunks;
+  la.rt_total = (int)rt_total;
+  if (fast) {
+    la.row0 = 0;
+    la.rtc = L.rt_chunk;
+    la.stats = (uint64_t*)(ws + L.stats);
     void* params[] = {&la};
-    if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(rtc * L.nvt)), dim3(256), params, lds_bytes, st) !=
-        hipSuccess)
+    if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(L.rt_chunk * L.nvt)), dim3(256), params, lds_bytes,
+                                   st) != hipSuccess)
       return CE_ERR_HIP;
+  } else {
+    for (int c = 0; c < L.nchunks; ++c) {
+      const int64_t rt0 = (int64_t)c * L.rt_chunk;
+      const int rtc = (int)((rt_total - rt0 < L.rt_chunk) ? rt_total - rt0 : L.rt_chunk);
+      la.row0 = rt0 * 256;
+      la.rtc = rtc;
+      la.stats = (uint64_t*)(ws + L.stats) + (size_t)c * L.rt_chunk * 256 * L.nvt * 2;
+      void* params[] = {&la};
+      if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(rtc * L.nvt)), dim3(256), params, lds_bytes,
+                                     st) != hipSuccess)
+        return CE_ERR_HIP;
+    }
   }
   if (gh) {  // dh [N, H] = g [N, V] W [V, H]
     BwdArgs b;

@@ -305,12 +305,15 @@ __device__ __forceinline__ void read_frags(const char* st, int wm, int wn, int l
 // The K loop of one 256 x 256 tile: acc = A[m0:, :] B[n0:, :]^T, A and B
 // of layouts AK / BKD (16-byte aligned rows; a KO operand's extent along
 // its tile dimension a whole number of 16-byte chunks or padded to one).
-// Needs kLdsBytes of LDS.
+// Needs kLdsBytes of LDS.  tid_: the thread index, when the caller runs tiles
+// in a loop and passes one the compiler cannot see through (so no
+// lane-dependent address is hoisted out of that loop and held across it);
+// threadIdx.x otherwise.
 template <typename T, int AK, int BKD, int S = STAGES>
 __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
-                                         int M, int N, int K, int m0, int n0) {
+                                         int M, int N, int K, int m0, int n0, int tid_ = -1) {
   static_assert(S >= 4, "the loads of a step go out two and three steps ahead");
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = tid_ < 0 ? (int)threadIdx.x : tid_, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   DmaOp<AK> oa;
@@ -388,8 +391,8 @@ __device__ __forceinline__ void tile_dma(Tile& t, char* lds, const char* A, int6
 
 template <typename T>
 __device__ __forceinline__ void tile_nt(Tile& t, char* lds, const char* A, int64_t lda, const char* B, int64_t ldb,
-                                        int M, int N, int K, int m0, int n0) {
-  tile_dma<T, kKC, kKC>(t, lds, A, lda, B, ldb, M, N, K, m0, n0);
+                                        int M, int N, int K, int m0, int n0, int tid = -1) {
+  tile_dma<T, kKC, kKC>(t, lds, A, lda, B, ldb, M, N, K, m0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------
