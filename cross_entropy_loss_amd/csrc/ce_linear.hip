@@ -296,6 +296,8 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
   int32_t* yrel = (int32_t*)(lds + 2048);   // [256] label column - n0 when in this tile, else -1
   float* mrow = (float*)(lds + 3072);       // [256] the tile's row max
   float* xyl = (float*)(lds + 4096);        // [256 + 64] label logits found here (+ junk slots)
+  float* mrowc = (float*)(lds + 6144);      // [256] the row max times log2 e (0 for -inf): the exponentials' shift
+  float* crow = (float*)(lds + 7168);       // [256] s 2^(mrowc - lse log2 e): g = e crow on a row's off-label elements
   float* lrow = (float*)(lds + 10240);      // [256] lse of the tile's rows
   float* prow = (float*)(lds + 11264);      // [256] 1 - p_y
   uint32_t* sflag = (uint32_t*)(lds + 12288);
@@ -347,55 +349,47 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
 #pragma unroll 8
     for (int q = 1; q < 64; ++q) m = fmaxf(m, pr[q]);
     mrow[tid] = m;
+    mrowc[tid] = (m == -INFINITY) ? 0.0f : m * kLog2e;
   }
   __syncthreads();
-  // pass B: the label-excluded sums relative to the row max; the lane that
-  // holds a row's label logit leaves it in xyl (others write a junk slot).
-  // A wave whose 32-row block holds no label of its columns (most blocks)
-  // sums without per-element tests.
+  // pass B: e = 2^(x log2 e - mc) for every element, written over its
+  // logit in the accumulators (the gradient pass multiplies it by the row's
+  // constant instead of taking a second exponential), and per lane and row
+  // the label-excluded sum of its four.  For a row whose label lies in some
+  // lane's columns (a ballot per row, rarely true) the lane that holds it
+  // takes out the label's logit (into xyl) and sets its e to 0; no other
+  // row pays a per-element label test.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float mc[16], sv[16], xv[16];
-    int lj[16];
-    bool lab = false;
+    float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = lg::acc_row(wm, i, v, lane);
-      const float mr = mrow[r];
-      mc[v] = (mr == -INFINITY) ? 0.0f : mr * kLog2e;
-      const int d = yrel[r] - lc;  // the label's column is this lane's in block d / 32
-      lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
-      lab = lab || lj[v] >= 0;
-      sv[v] = 0.0f;
-      xv[v] = 0.0f;
-    }
-    if (full && __ballot(lab) == 0) {
+      const float mc = mrowc[r];
+      float e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x16 blk = t.acc[i][j];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sv[v] += __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -mc));
+        if (!full) e[j] = cvalid[j] ? e[j] : 0.0f;
       }
+      const int d = yrel[r] - lc;         // the label's column is this lane's in block d / 32
+      const bool own = (d & ~0x60) == 0;  // d in {0, 32, 64, 96}
+      if (__ballot(own) != 0) {
+        float xv = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part_l[kRowOff(i, v) * kPS] = sv[v];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16 blk = t.acc[i][j];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -mc[v]));
-          sv[v] += (cvalid[j] && lj[v] != j) ? e : 0.0f;
-          xv[v] = (lj[v] == j) ? blk[v] : xv[v];
+        for (int j = 0; j < 4; ++j) {
+          const bool hit = own && (d >> 5) == j;
+          xv = hit ? t.acc[i][j][v] : xv;
+          e[j] = hit ? 0.0f : e[j];
         }
+        if (own) xyl[r] = xv;
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = lg::acc_row(wm, i, v, lane);
-        part_l[kRowOff(i, v) * kPS] = sv[v];
-        xyl[(lj[v] >= 0) ? r : 256 + lane] = xv[v];
-      }
+      for (int j = 0; j < 4; ++j) t.acc[i][j][v] = e[j];
+      sv[v] = (e[0] + e[1]) + (e[2] + e[3]);
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part_l[kRowOff(i, v) * kPS] = sv[v];
   }
   __syncthreads();
   {
@@ -480,24 +474,25 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
     }
     lrow[r] = l;
     prow[r] = pcv;
+    crow[r] = gs * __builtin_amdgcn_exp2f(mrowc[r] - l * kLog2e);
   }
   if (to) atomicOr(sflag, 1u);
   __syncthreads();
   if (tid == 0 && sflag[0]) atomicOr(&a.hdr->status, kStatusSyncTimeout);
   const bool bad_scale = sflag[0] != 0u;
 
-  // g from the accumulators: s 2^((x - lse) log2 e) off the label,
-  // -s (1 - p_y) on it, +0 on ignored rows and past the vocabulary, NaN on
-  // rows with a label outside [0, V).  Each wave stages its 128 x 128
-  // quarter in LDS (rows of 272 bytes) and writes it out as 16-byte vectors.
-  const float lgs = (gs > 0.0f) ? log2f(gs) : 0.0f;
+  // g from the accumulators (which now hold e = 2^(x log2 e - mc)):
+  // s 2^((x - lse) log2 e) = e crow off the label, -s (1 - p_y) on it, +0 on
+  // ignored rows and past the vocabulary, NaN on rows with a label outside
+  // [0, V).  Each wave stages its 128 x 128 quarter in LDS (rows of 272
+  // bytes) and writes it out as 16-byte vectors.
   constexpr int kGS = 136;  // staged row stride in elements
   __syncthreads();  // the statistics area is free
   uint16_t* stg = (uint16_t*)(lds + 16384 + wave * (128 * kGS * 2));
-  // The common case (a full tile, s > 0, every exchange in time) writes
-  // 2^(x log2 e - b) everywhere, then fixes up the few special elements:
-  // the label's, ignored rows (+0) and rows with a bad label (NaN).
-  const bool fast = full && gs > 0.0f && !bad_scale;
+  // The common case (a full tile, every exchange in time) writes e crow
+  // everywhere, then fixes up the few special elements: the label's,
+  // ignored rows (+0) and rows with a bad label (NaN).
+  const bool fast = full && !bad_scale;
   const int64_t cbase = (int64_t)n0 + wn * 128;
   if (fast) {
     uint16_t* stg_l = stg + 4 * (lane >> 5) * kGS + (lane & 31);  // + kRowOff(i, v) * kGS + 32 j
@@ -506,15 +501,14 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
     // stores of one block overlap the arithmetic of the next
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float bv[16];
+      float cr[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) bv[v] = lrow[lg::acc_row(wm, i, v, lane)] * kLog2e - lgs;
+      for (int v = 0; v < 16; ++v) cr[v] = crow[lg::acc_row(wm, i, v, lane)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16 blk = t.acc[i][j];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])));
+        for (int v = 0; v < 16; ++v) stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(blk[v] * cr[v]);
       }
       // fix-ups of rows 32 i .. 32 i + 31, after this wave's own staged
       // writes (LDS keeps a wave's order): the label's element, ignored rows
@@ -545,7 +539,7 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float bv[16], gyv[16], mul[16];
+      float cr[16], gyv[16];
       int lj[16], kind[16];  // kind: 0 normal, 1 zero (ignored row), 2 NaN (bad label or failed exchange)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -553,9 +547,7 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
         const int64_t y = ys[r];
         const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
         kind[v] = ign ? 1 : ((bad || bad_scale) ? 2 : 0);
-        // g = 2^(x log2 e - b) * mul: b folds log2 s in when s > 0
-        bv[v] = lrow[r] * kLog2e - (gs > 0.0f ? lgs : 0.0f);
-        mul[v] = (gs > 0.0f) ? 1.0f : gs;
+        cr[v] = crow[r];
         gyv[v] = -gs * prow[r];
         const int d = yrel[r] - lc;
         lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
@@ -565,7 +557,7 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
         const f32x16 blk = t.acc[i][j];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float gv = __builtin_amdgcn_exp2f(__builtin_fmaf(blk[v], kLog2e, -bv[v])) * mul[v];
+          float gv = blk[v] * cr[v];
           gv = (lj[v] == j) ? gyv[v] : gv;
           gv = (kind[v] == 2) ? __builtin_nanf("") : gv;
           gv = (kind[v] == 1 || !cvalid[j]) ? 0.0f : gv;
