@@ -27,8 +27,12 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a device pointer owned by the caller; the
- *     library allocates no memory and keeps no pointer after return (the
- *     LM-head entry point's GEMM libraries are the one exception, see there).
+ *     library allocates no memory and keeps no pointer after return.
+ *   - The library links the HIP runtime and nothing else.  In a process that
+ *     also uses PyTorch (which ships its own copy of the runtime), load this
+ *     library after PyTorch: loaded first, it brings up the system runtime,
+ *     in which PyTorch's device pointers are not valid (a launch then fails
+ *     with CE_ERR_HIP).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
  *     stream).  No entry point synchronises the stream or reads device data on
  *     the host; outputs are valid once the stream work completes, and inputs
