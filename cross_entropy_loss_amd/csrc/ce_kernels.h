@@ -902,7 +902,7 @@ __global__ __launch_bounds__(NT, (row_min_waves<NT, VPL>())) void row_kernel_16(
   __shared__ float lds_m[NW], lds_s[NW], lds_mn[NW];
   __shared__ uint32_t lds_u[2 * NW + 4];
   __shared__ double lds_d[NT];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
 
   const uint32_t epoch = ld_agent(&a.ws->epoch);  // unchanged until the finisher's last store
@@ -1045,7 +1045,7 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
   __shared__ float lds_m[2][NW], lds_s[2][NW], lds_mn[2][NW];
   __shared__ uint32_t lds_u[2 * NW + 4];
   __shared__ double lds_d[NT];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t G = gridDim.x;
   const int nvec = (int)(a.V / EPV);
   const uint32_t rbytes = (uint32_t)nvec * 16u;
@@ -1053,7 +1053,7 @@ __global__ __launch_bounds__(NT, 4) void row_fused_aligned(Args a) {
 
   const uint32_t epoch = ld_agent(&a.ws->epoch);
   const uint32_t tag = epoch + 1u;
-  if (blockIdx.x < a.K) count_and_publish<NT>(a, (int)blockIdx.x, tag, lds_u + 4);
+  if ((int)blockIdx.x < a.K) count_and_publish<NT>(a, (int)blockIdx.x, tag, lds_u + 4);
 
   poll_to_lds(a, tag, lds_u);
   int par = 0;

@@ -268,7 +268,7 @@ struct DmaOp<kKO> {
   // block rows mb .. mb + 31 (mb a multiple of 32): the lane's chunk is
   // mb / 8 + cl, whose slot is (mb / 8 + cl) ^ swz = (mb / 8) ^ cx (mb / 8 is a
   // multiple of 4 and cl < 4, so the sum is an XOR)
-  __device__ __forceinline__ u32x4 frag_of(const char* slab, int mb, int kk, int lane) const {
+  __device__ __forceinline__ u32x4 frag_of(const char* slab, int mb, int kk, int /* lane: in rd, cx */) const {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const uint32_t a = rd + ((((uint32_t)mb >> 3) ^ cx) << 4) + (uint32_t)kk * (16 * 512);
