@@ -136,7 +136,7 @@ def _db_rows(path, sql):
 def profile_summary_linear(d: str, workload: int) -> None:
     """Kernel-trace summary of the LM-head path (bench.py --op linear) ->
     profiles/ce_linear_<workload>.txt: per kernel the time per call, and for
-    the three matrix-product kernels (logits + cross-entropy epilogue, dh,
+    the three matrix-product kernels (logits with the tile statistics, dh,
     dW) their rate over 2 N H V flops each.  The two backward launches of a
     call are told apart by their order (dh, then dW)."""
     import glob
@@ -156,8 +156,10 @@ def profile_summary_linear(d: str, workload: int) -> None:
         if "lin_prep_kernel" in name:
             bwd_seen = 0
             label = "lin_prep_kernel (labels, counts)"
-        elif "lin_logits_ce_kernel" in name:
-            label = "lin_logits_ce_kernel (logits = h W^T + cross-entropy epilogue, all chunks)"
+        elif "lin_logits_kernel" in name:
+            label = "lin_logits_kernel (logits = h W^T, tile statistics and exponentials)"
+        elif "lin_rescale_kernel" in name:
+            label = "lin_rescale_kernel (row log-sum-exp, loss, g over the exponentials)"
         elif "lin_bwd_kernel" in name:
             label = ("lin_bwd_kernel dh = g W" if bwd_seen == 0 else "lin_bwd_kernel dW = g^T h")
             bwd_seen += 1
@@ -181,7 +183,7 @@ def profile_summary_linear(d: str, workload: int) -> None:
         per_call = s_ / calls / 1e6
         total += per_call
         rate = ""
-        if label.startswith(("lin_logits_ce_kernel", "lin_bwd_kernel")):
+        if label.startswith(("lin_logits_kernel", "lin_bwd_kernel")):
             rate = f"{flops_per_gemm / (per_call * 1e-3) / 1e12:8.0f}"
         lines.append(f"  {label:76s} {n // calls:8d} {per_call:9.3f} {rate:>8s}")
     lines.append(f"  {'total':76s} {'':8s} {total:9.3f} {3 * flops_per_gemm / (total * 1e-3) / 1e12:8.0f}")

@@ -11,25 +11,24 @@
 //   dL/dh = g W,   dL/dW = g^T h,   g = dloss * dL/dlogits.
 //
 // bf16 / fp16 (all three products on the matrix cores, lin_gemm.h):
-//   1. prep: n_valid, the gradient scale s = dloss 2^k / n_valid (fp16 keeps
-//      g in its normal range through 2^k, k = 14 - ilogb(dloss / n); bf16
-//      k = 0), and a new epoch tag for the call.
-//   2. logits + cross-entropy, cooperative, in chunks of rows: each
-//      workgroup holds one 256 x 256 logits tile in its fp32 accumulators, so
-//      no logits ever reach memory.  From the registers it takes per row the
-//      tile's (max, sum of exp without the label column), publishes them as
-//      epoch-tagged words, merges the rows it owns (every tile of a row is
-//      resident at once: the chunk's grid is sized to be co-resident and
-//      launched cooperatively), publishes lse and 1 - p_y, and then writes
-//      the gradient tile g = s (softmax - onehot) in the input format straight
-//      from its accumulators -- the per-chunk log-sum-exp merge of a chunked
-//      loss, done across workgroups.
-//   3. dh = g W        MFMA, g K-contiguous, W read K-outer (transposed on its
+//   1. prep: n_valid and the gradient scale s = dloss 2^k / n_valid (fp16
+//      keeps g in its normal range through 2^k, k = 14 - ilogb(dloss / n);
+//      bf16 k = 0).
+//   2. logits: one workgroup per 256 x 256 tile of h W^T in fp32
+//      accumulators; no logits reach memory.  Its epilogue takes per row the
+//      tile's max and stores the tile's exponentials relative to it, in the
+//      input format, where g will be, with the row's (shift, label-excluded
+//      sum) for the tile and the label's logit -- the per-chunk statistics of
+//      a chunked loss, with 256-column chunks.
+//   3. per row: the tiles' statistics merged into the log-sum-exp, the loss,
+//      and g = s (softmax - onehot) written over the exponentials (each
+//      scaled by its tile's factor, rounded to the input format).
+//   4. dh = g W        MFMA, g K-contiguous, W read K-outer (transposed on its
 //                      way into LDS); scaled by 2^-k on output
-//   4. dW = g^T h      MFMA, both read K-outer; scaled by 2^-k on output
-//   5. the token mean over the batch, summed in row order in fp64.
-// The workspace holds g (N x V in the input format) and the small tagged
-// exchange arrays; no fp32 logits and no transposed copies.
+//   5. dW = g^T h      MFMA, both read K-outer; scaled by 2^-k on output
+//   6. the token mean over the batch, summed in row order in fp64.
+// The workspace holds g (N x V in the input format) and per row and tile two
+// floats; no fp32 logits and no transposed copies.
 //
 // fp32 inputs: the same steps with a plain tiled fp32 GEMM (no MFMA) and the
 // chunk's fp32 logits in the workspace, reduced by the cross-entropy kernels
@@ -50,7 +49,6 @@ using lg::Tile;
 constexpr int kNT = 1024;               // prep / finish kernels
 constexpr int64_t kMaxChunks = 4096;    // per-chunk counts live in LDS (fp32 path)
 constexpr int64_t kF32ChunkRows = 1024;  // fp32 path default
-constexpr int kSpinLimit = 1 << 20;      // polls before an exchange wait gives up
 constexpr uint32_t kStatusLabelRange = 0x1u, kStatusSyncTimeout = 0x2u;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -62,89 +60,34 @@ bool fits32(int64_t x) { return x >= 0 && x < ((int64_t)1 << 31); }
 // Workspace of the 16-bit path.
 // ---------------------------------------------------------------------------
 struct LinHeader {
-  uint32_t epoch;   // bumped by prep: this call's tag
   uint32_t status;  // status bits of this call (cleared by prep)
   float gscale;     // s = dloss 2^k / n_valid
   float unscale;    // 2^-k
   int32_t n_valid;
-  uint32_t pad[59];
+  uint32_t pad[60];
 };
 static_assert(sizeof(LinHeader) == 256, "header size");
 
 struct FastLayout {
-  size_t g, stats, xy, lse, pc, total;
-  int64_t ldg;    // g's row stride: vocab rounded up to 8 elements
-  int nvt;        // vocabulary tiles of 256
-  int rt_chunk;   // row tiles per chunk
-  int nchunks;
+  size_t g, tstats, xy, total;
+  int64_t ldg;  // g's row stride: vocab rounded up to 8 elements
+  int nvt;      // vocabulary tiles of 256
 };
 
-// Row tiles per cooperative chunk: every tile of the chunk resident at once.
-FastLayout fast_layout(int64_t N, int64_t V, int64_t resident) {
+FastLayout fast_layout(int64_t N, int64_t V) {
   FastLayout L;
   memset(&L, 0, sizeof(L));
   L.ldg = (V + 7) / 8 * 8;
   L.nvt = (int)((V + 255) / 256);
-  const int64_t rt_total = (N + 255) / 256;
-  int64_t rc = resident / L.nvt;
-  if (rc < 1) rc = 1;
-  if (rc > rt_total) rc = rt_total > 0 ? rt_total : 1;
-  L.rt_chunk = (int)rc;
-  L.nchunks = (int)((rt_total + rc - 1) / rc);
   size_t off = sizeof(LinHeader);
   L.g = align256(off);
   off = L.g + align256((size_t)N * L.ldg * 2);
-  L.stats = off;  // [chunk][row in chunk][vocab tile] x 2 tagged words
-  off += align256((size_t)(L.nchunks > 0 ? L.nchunks : 1) * rc * 256 * L.nvt * 16);
-  L.xy = off;
-  off += align256((size_t)N * 8);
-  L.lse = off;
-  off += align256((size_t)N * 8);
-  L.pc = off;
-  off += align256((size_t)N * 8);
+  L.tstats = off;  // [row][vocabulary tile]: (c, sum) float pairs
+  off += align256((size_t)N * L.nvt * 8);
+  L.xy = off;  // [row] the label's logit
+  off += align256((size_t)N * 4);
   L.total = off;
   return L;
-}
-
-// Co-resident workgroups of the 16-bit logits kernel: one per CU (its LDS
-// and accumulator registers fill a CU).  Taken as the device's CU count.
-int64_t device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return cus;
-}
-
-// ---------------------------------------------------------------------------
-// Tagged exchange words: tag << 32 | float bits, one relaxed agent-scope
-// 64-bit store / load each (the reader polls until the tag is this call's).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t tag, float v) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-// Polls *p until it carries `tag`; on timeout returns NaN and sets *to.
-__device__ __forceinline__ float get_tagged(const uint64_t* p, uint32_t tag, uint32_t& to) {
-  for (int it = 0;; ++it) {
-    const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == tag) return __builtin_bit_cast(float, (uint32_t)w);
-    if (to || it >= kSpinLimit) {
-      to = 1;
-      return __builtin_nanf("");
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// A tagged word's load, and its value once loaded (polled for when the word
-// is not yet this call's): a thread issues all its loads before it checks
-// any, so the exchange costs one round trip rather than one per word.
-__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float tagged_value(uint64_t w, const uint64_t* p, uint32_t tag, uint32_t& to) {
-  if ((uint32_t)(w >> 32) == tag) return __builtin_bit_cast(float, (uint32_t)w);
-  return get_tagged(p, tag, to);
 }
 
 // Whole-wave max / sum (every lane gets the result; fixed order).
@@ -173,7 +116,7 @@ __device__ __forceinline__ uint16_t to_bits<_Float16>(float x) {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// 1. prep (one workgroup): n_valid, the scale, the epoch; for the fp32 path
+// 1. prep (one workgroup): n_valid and the scale; for the fp32 path
 // also each chunk's dloss share.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, int64_t N, int64_t ignore, int64_t T,
@@ -215,7 +158,6 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
   if (tid == 0) {
     n_valid_out[0] = (int32_t)n;
     if (hdr) {
-      hdr->epoch = hdr->epoch + 1u;
       hdr->status = 0u;
       hdr->gscale = n > 0 ? (float)(dl * up / (double)n) : 0.0f;
       hdr->unscale = (float)ldexp(1.0, -k);
@@ -225,9 +167,16 @@ __global__ __launch_bounds__(kNT) void lin_prep_kernel(const int64_t* labels, in
 }
 
 // ---------------------------------------------------------------------------
-// 2. logits tile + cross-entropy epilogue (16-bit; cooperative launches over
-// chunks of row tiles).  Grid: rt x nvt workgroups in the XCD order, so the
-// row tiles that share a weight slab run on one XCD.
+// 2. logits tile + the tile's share of the cross-entropy (16-bit).  One
+// workgroup per 256 x 256 tile of logits = h W^T, over a plain grid of every
+// tile (no co-residency, no exchange between workgroups).  From its fp32
+// accumulators the epilogue takes per row the tile's max m over the columns
+// inside the vocabulary and writes, into g's place, in the input format,
+//   e = 2^(x log2 e - c),  c = m log2 e - E   (E = 14 for fp16, else 0:
+//                                              fp16 keeps e in its normal range)
+// with 0 at the label's column (the label's logit goes to xy), and per row
+// the pair (c, sum of the tile's e).  The row's log-sum-exp needs every tile
+// of the row, so the scale that turns e into g comes in the next kernel.
 // ---------------------------------------------------------------------------
 struct LogitsArgs {
   const char* h;
@@ -237,79 +186,74 @@ struct LogitsArgs {
   const int64_t* labels;
   int64_t ignore;
   int64_t N, H, V;
-  int64_t row0;  // first row of this chunk
-  int rtc;       // row tiles in this chunk
-  int nvt;
-  int rt_chunk, nchunks, rt_total;  // row tiles per chunk, chunks, row tiles in all
-  LinHeader* hdr;
+  int mt, nvt;     // row tiles, vocabulary tiles
+  float eshift;    // E
   uint16_t* g;
   int64_t ldg;
-  uint64_t* stats;  // this chunk's [rtc * 256][nvt][2] (every chunk's in the one-launch form)
-  uint64_t* xy;     // [N]
-  uint64_t* lse;    // [N]
-  uint64_t* pc;     // [N]
-  float* loss_rows;
+  float2* tstats;  // [N][nvt]: (c, sum of e); c = -inf for a row with no finite max in the tile
+  float* xy;       // [N]: the label's logit (written by the tile that holds it)
 };
 
-// LDS: the K loop's stages (128 KB or 64 KB), then the epilogue's statistics
-// (16 KB + a 72 KB transpose area) and four staged 128 x 136 gradient
-// quarters (136 KB) at offset 16 KB: all of a CU's 160 KB.
+// LDS: the K loop's stages (128 KB, or 64 KB for the element-wise loop),
+// then the epilogue's row data (4 KB), its statistics transpose (65 KB at
+// offset 16 KB) and, after it, four staged 128 x 136 quarters of e (136 KB
+// at offset 16 KB).
 constexpr int kLogitsLds = 160 * 1024;
-static_assert(16384 + 4 * 128 * 136 * 2 <= kLogitsLds, "staged gradient quarters");
+static_assert(16384 + 4 * 128 * 136 * 2 <= kLogitsLds, "staged quarters");
 static_assert(16384 + 256 * 65 * 4 <= kLogitsLds, "statistics transpose");
 
 // Row of accumulator element v of 32-row block i within a lane's rows (the
 // lane's first row is wm * 128 + 4 * (lane / 32); see lg::acc_row).
 __device__ constexpr int kRowOff(int i, int v) { return i * 32 + 8 * (v >> 2) + (v & 3); }
-// Tiles per lane and round of the row merge (128 tiles a round).
-constexpr int kMergeQ = 2;
 
-template <typename T, bool DMA, int AK, int BKD>
-// One tile of one chunk: workgroup blockIdx.x of a grid of rtg x nvt takes
-// tile (rt, vt) of the chunk (none when rt is past the chunk's rtc row tiles).
-// tid is the thread index (opaque to the compiler in the one-launch loop).
-__device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, int tid, int rtg) {
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
-  // the row tiles that share a weight slab are neighbours in the XCD order,
-  // so they run on one XCD and the slab is fetched into its L2 once
-  const int lin = lg::xcd_order((int)blockIdx.x, rtg * a.nvt);
-  const int rt = lin % rtg, vt = lin / rtg;
-  if (rt >= a.rtc) return;  // the last chunk may have fewer row tiles
-  const int64_t mrow0 = a.row0 + (int64_t)rt * 256;  // the tile's first row (global)
+// Row tiles per group of the tile order (8 and 4 measured alike at 4096 x
+// 4096 x 32000, 16 about 2% slower per call).
+constexpr int kRowGroup = 8;
+
+// Tile order: groups of kRowGroup row tiles; inside a group the tiles walk
+// the vocabulary slab by slab with the group's row tiles of a slab adjacent.
+// In the XCD order each XCD takes one contiguous stretch of that walk, so the
+// row tiles that share a weight slab run on one XCD at about the same time
+// and the slab comes into that XCD's L2 once.
+__device__ __forceinline__ void logits_tile_of(int bid, int mt, int nvt, int& rt, int& vt) {
+  const int lin = lg::xcd_order(bid, mt * nvt);
+  const int grp = lin / (kRowGroup * nvt), idx = lin - grp * (kRowGroup * nvt);
+  const int rows = min(kRowGroup, mt - grp * kRowGroup);
+  rt = grp * kRowGroup + idx % rows;
+  vt = idx / rows;
+}
+
+template <typename T, bool DMA>
+__global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int rt, vt;
+  logits_tile_of((int)blockIdx.x, a.mt, a.nvt, rt, vt);
+  const int64_t mrow0 = (int64_t)rt * 256;  // the tile's first row
   const int n0 = vt * 256;
   const int M = (int)a.N, Nv = (int)a.V, K = (int)a.H;
   Tile t;
-  if constexpr (DMA) lg::tile_nt<T>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0, tid);
-  else lg::tile_rs<T, AK, BKD>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
-  const uint32_t tag = a.hdr->epoch;
-  const float gs = a.hdr->gscale;
+  if constexpr (DMA) lg::tile_nt<T>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
+  else lg::tile_rs<T, lg::kKCg, lg::kKCg>(t, lds, a.h, a.ldh, a.w, a.ldw, M, Nv, K, (int)mrow0, n0);
   __syncthreads();  // every wave is done with the K loop's LDS
 
   // LDS after the K loop: per-row label data and statistics, and a
   // [256][kPS] transpose area for the per-lane partials (kPS = 65 floats per
   // row: the row reductions, one thread per row, read without bank
-  // conflicts; the half-waves' writes, four rows apart, overlap on 28 banks).  The
-  // epilogue walks the accumulators one 32-row block (index i) at a time so
-  // that only that block's row constants are held in registers.
+  // conflicts).  The passes walk the accumulators one 32-row block (index i)
+  // at a time so that only that block's row constants are held in registers.
   constexpr int kPS = 65;
-  int64_t* ys = (int64_t*)lds;              // [256] labels of the tile's rows
-  int32_t* yrel = (int32_t*)(lds + 2048);   // [256] label column - n0 when in this tile, else -1
-  float* mrow = (float*)(lds + 3072);       // [256] the tile's row max
-  float* xyl = (float*)(lds + 4096);        // [256 + 64] label logits found here (+ junk slots)
-  float* mrowc = (float*)(lds + 6144);      // [256] the row max times log2 e (0 for -inf): the exponentials' shift
-  float* crow = (float*)(lds + 7168);       // [256] s 2^(mrowc - lse log2 e): g = e crow on a row's off-label elements
-  float* lrow = (float*)(lds + 10240);      // [256] lse of the tile's rows
-  float* prow = (float*)(lds + 11264);      // [256] 1 - p_y
-  uint32_t* sflag = (uint32_t*)(lds + 12288);
-  float* part = (float*)(lds + 16384);      // [256][kPS]
-  if (tid == 0) sflag[0] = 0u;
+  int32_t* yrel = (int32_t*)lds;        // [256] label column - n0 when in this tile, else -1
+  float* mrow = (float*)(lds + 1024);   // [256] the tile's row max
+  float* mrowc = (float*)(lds + 2048);  // [256] c (0 for a row whose max is -inf): the exponentials' shift
+  float* xyl = (float*)(lds + 3072);    // [256] label logits found here
+  float* part = (float*)(lds + 16384);  // [256][kPS]
   {
     const int64_t R = mrow0 + tid;
     const int64_t y = (R < a.N) ? a.labels[R] : a.ignore;
-    ys[tid] = y;
     yrel[tid] = (y != a.ignore && y >= n0 && y < n0 + 256 && y < a.V) ? (int)(y - n0) : -1;
   }
-  __syncthreads();
   const int lc = wn * 128 + (lane & 31);  // this lane's column in block j: lc + 32 j
   bool cvalid[4];
 #pragma unroll
@@ -349,16 +293,15 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
 #pragma unroll 8
     for (int q = 1; q < 64; ++q) m = fmaxf(m, pr[q]);
     mrow[tid] = m;
-    mrowc[tid] = (m == -INFINITY) ? 0.0f : m * kLog2e;
+    mrowc[tid] = (m == -INFINITY) ? 0.0f : m * kLog2e - a.eshift;
   }
   __syncthreads();
-  // pass B: e = 2^(x log2 e - mc) for every element, written over its
-  // logit in the accumulators (the gradient pass multiplies it by the row's
-  // constant instead of taking a second exponential), and per lane and row
-  // the label-excluded sum of its four.  For a row whose label lies in some
-  // lane's columns (a ballot per row, rarely true) the lane that holds it
-  // takes out the label's logit (into xyl) and sets its e to 0; no other
-  // row pays a per-element label test.
+  // pass B: e = 2^(x log2 e - c) for every element, written over its logit
+  // in the accumulators, and per lane and row the label-excluded sum of its
+  // four.  For a row whose label lies in some lane's columns (a ballot per
+  // row, rarely true) the lane that holds it takes out the label's logit
+  // (into xyl) and sets its e to 0; no other row pays a per-element label
+  // test.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float sv[16];
@@ -398,220 +341,172 @@ __device__ __forceinline__ void logits_ce_tile(const LogitsArgs& a, char* lds, i
     float S = 0.0f;
 #pragma unroll 8
     for (int q = 0; q < 64; ++q) S += pr[q];
-    if (mrow0 + r < a.N) {
-      uint64_t* sp = a.stats + ((size_t)(rt * 256 + r) * a.nvt + vt) * 2;
-      put_tagged(sp, tag, mrow[r]);
-      put_tagged(sp + 1, tag, S);
-      if (yrel[r] >= 0) put_tagged(a.xy + mrow0 + r, tag, xyl[r]);
+    const int64_t R = mrow0 + r;
+    if (R < a.N) {
+      a.tstats[R * a.nvt + vt] = make_float2(mrow[r] == -INFINITY ? -INFINITY : mrowc[r], S);
+      if (yrel[r] >= 0) a.xy[R] = xyl[r];
     }
   }
-
-  // rows r = vt, vt + nvt, ... of this row tile are merged here, one wave per
-  // row: its lanes fetch the nvt tiles' (max, sum) words (all loads issued
-  // before any is waited on), merge their own, and the wave merges the lanes
-  uint32_t to = 0;
-  for (int k = wave;; k += 4) {
-    const int r = vt + k * a.nvt;
-    if (r >= 256 || mrow0 + r >= a.N) break;
-    const int64_t R = mrow0 + r, y = ys[r];
-    float loss = 0.0f;
-    if (y != a.ignore) {
-      if (y < 0 || y >= a.V) {
-        loss = __builtin_nanf("");
-      } else {
-        const uint64_t* sp = a.stats + (size_t)(rt * 256 + r) * a.nvt * 2;
-        const uint64_t wxy = ld_tagged(a.xy + R);
-        float ml = -INFINITY, sl = 0.0f;  // this lane's running (max, sum)
-        for (int v0 = 0; v0 < a.nvt; v0 += 64 * kMergeQ) {
-          uint64_t wm_[kMergeQ], ws_[kMergeQ];
-#pragma unroll
-          for (int q = 0; q < kMergeQ; ++q) {
-            const int v2 = v0 + lane + 64 * q;
-            if (v2 < a.nvt) {
-              wm_[q] = ld_tagged(sp + v2 * 2);
-              ws_[q] = ld_tagged(sp + v2 * 2 + 1);
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < kMergeQ; ++q) {
-            const int v2 = v0 + lane + 64 * q;
-            if (v2 < a.nvt) {
-              const float mv = tagged_value(wm_[q], sp + v2 * 2, tag, to);
-              const float sv = tagged_value(ws_[q], sp + v2 * 2 + 1, tag, to);
-              if (mv != -INFINITY) {
-                const float mn = fmaxf(ml, mv);
-                sl = ((ml == -INFINITY) ? 0.0f : sl * __builtin_amdgcn_exp2f((ml - mn) * kLog2e)) +
-                     sv * __builtin_amdgcn_exp2f((mv - mn) * kLog2e);
-                ml = mn;
-              }
-            }
-          }
-        }
-        const float Mx = wave_max(ml);
-        const float S = wave_sum((ml == -INFINITY) ? 0.0f : sl * __builtin_amdgcn_exp2f((ml - Mx) * kLog2e));
-        const float xy = tagged_value(wxy, a.xy + R, tag, to);
-        const float ey = __builtin_amdgcn_exp2f((xy - Mx) * kLog2e);
-        const float St = S + ey;
-        const float l = Mx + logf(St), pcomp = S / St;
-        loss = (pcomp >= 0.5f) ? (l - xy) : log1pf(S / ey);
-        if (lane == 0) {
-          put_tagged(a.lse + R, tag, l);
-          put_tagged(a.pc + R, tag, pcomp);
-        }
-      }
-    }
-    if (lane == 0) a.loss_rows[R] = loss;
-  }
-  // every row of the tile: its lse and 1 - p_y
-  {
-    const int r = tid;
-    const int64_t R = mrow0 + r, y = ys[r];
-    float l = 0.0f, pcv = 0.0f;
-    if (R < a.N && y != a.ignore && y >= 0 && y < a.V) {
-      const uint64_t wl = ld_tagged(a.lse + R), wp = ld_tagged(a.pc + R);
-      l = tagged_value(wl, a.lse + R, tag, to);
-      pcv = tagged_value(wp, a.pc + R, tag, to);
-    }
-    lrow[r] = l;
-    prow[r] = pcv;
-    crow[r] = gs * __builtin_amdgcn_exp2f(mrowc[r] - l * kLog2e);
-  }
-  if (to) atomicOr(sflag, 1u);
-  __syncthreads();
-  if (tid == 0 && sflag[0]) atomicOr(&a.hdr->status, kStatusSyncTimeout);
-  const bool bad_scale = sflag[0] != 0u;
-
-  // g from the accumulators (which now hold e = 2^(x log2 e - mc)):
-  // s 2^((x - lse) log2 e) = e crow off the label, -s (1 - p_y) on it, +0 on
-  // ignored rows and past the vocabulary, NaN on rows with a label outside
-  // [0, V).  Each wave stages its 128 x 128 quarter in LDS (rows of 272
-  // bytes) and writes it out as 16-byte vectors.
-  constexpr int kGS = 136;  // staged row stride in elements
   __syncthreads();  // the statistics area is free
-  uint16_t* stg = (uint16_t*)(lds + 16384 + wave * (128 * kGS * 2));
-  // The common case (a full tile, every exchange in time) writes e crow
-  // everywhere, then fixes up the few special elements: the label's,
-  // ignored rows (+0) and rows with a bad label (NaN).
-  const bool fast = full && !bad_scale;
-  const int64_t cbase = (int64_t)n0 + wn * 128;
-  if (fast) {
-    uint16_t* stg_l = stg + 4 * (lane >> 5) * kGS + (lane & 31);  // + kRowOff(i, v) * kGS + 32 j
-    const uint32_t nanb = to_bits<T>(__builtin_nanf("")), nan2 = (nanb << 16) | nanb;
-    // 32 rows of the quarter at a time: computed, fixed up and stored, so the
-    // stores of one block overlap the arithmetic of the next
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float cr[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) cr[v] = crow[lg::acc_row(wm, i, v, lane)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16 blk = t.acc[i][j];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(blk[v] * cr[v]);
-      }
-      // fix-ups of rows 32 i .. 32 i + 31, after this wave's own staged
-      // writes (LDS keeps a wave's order): the label's element, ignored rows
-      // (+0), rows with a bad label (NaN)
-      {
-        const int rq = i * 32 + (lane & 31), r = wm * 128 + rq;
-        const int64_t y = ys[r];
-        const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
-        const uint64_t zb = __ballot(lane < 32 && ign), nb = __ballot(lane < 32 && bad);
-        const int d = yrel[r] - wn * 128;  // the label's column in this quarter
-        if (lane < 32 && !ign && !bad && d >= 0 && d < 128) stg[rq * kGS + d] = to_bits<T>(-gs * prow[r]);
-        for (uint64_t b = zb; b; b &= b - 1) ((uint32_t*)(stg + (i * 32 + __builtin_ctzll(b)) * kGS))[lane] = 0u;
-        for (uint64_t b = nb; b; b &= b - 1) ((uint32_t*)(stg + (i * 32 + __builtin_ctzll(b)) * kGS))[lane] = nan2;
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int rr = i * 32 + q * 4 + (lane >> 4), cv = (lane & 15) * 8;
-        const int64_t R = mrow0 + wm * 128 + rr;
-        const int64_t c = cbase + cv;
-        if (R < a.N && c < a.ldg) {
-          const lg::u32x4 val = *(const lg::u32x4*)(stg + rr * kGS + cv);
-          *(lg::u32x4*)(a.g + R * a.ldg + c) = val;
-        }
-      }
-    }
-    return;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float cr[16], gyv[16];
-      int lj[16], kind[16];  // kind: 0 normal, 1 zero (ignored row), 2 NaN (bad label or failed exchange)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = lg::acc_row(wm, i, v, lane);
-        const int64_t y = ys[r];
-        const bool ign = (y == a.ignore), bad = !ign && (y < 0 || y >= a.V);
-        kind[v] = ign ? 1 : ((bad || bad_scale) ? 2 : 0);
-        cr[v] = crow[r];
-        gyv[v] = -gs * prow[r];
-        const int d = yrel[r] - lc;
-        lj[v] = (d >= 0 && d < 128 && (d & 31) == 0) ? (d >> 5) : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16 blk = t.acc[i][j];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float gv = blk[v] * cr[v];
-          gv = (lj[v] == j) ? gyv[v] : gv;
-          gv = (kind[v] == 2) ? __builtin_nanf("") : gv;
-          gv = (kind[v] == 1 || !cvalid[j]) ? 0.0f : gv;
-          const int r = lg::acc_row(wm, i, v, lane);
-          stg[(r - wm * 128) * kGS + (lc - wn * 128) + 32 * j] = to_bits<T>(gv);
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
-  // 128 rows x 16 vectors of the quarter: four rows per pass of the wave
-#pragma unroll 4
-  for (int q = 0; q < 32; ++q) {
-    const int rr = q * 4 + (lane >> 4), cv = (lane & 15) * 8;
-    const int64_t R = mrow0 + wm * 128 + rr;
-    const int64_t c = cbase + cv;
-    if (R < a.N && c < a.ldg) {
-      const lg::u32x4 val = *(const lg::u32x4*)(stg + rr * kGS + cv);
-      *(lg::u32x4*)(a.g + R * a.ldg + c) = val;
-    }
-  }
-}
 
-// The direct-to-LDS form walks every chunk in one cooperative launch: each
-// workgroup takes tile (rt, vt) of chunk 0, 1, ... in turn.  The row tiles of
-// a chunk exchange their statistics through slots of their own and every
-// workgroup walks the chunks in the same order, so the waits of chunk c only
-// involve workgroups that reach chunk c.  (One cooperative launch per chunk
-// leaves the GPU idle ~19 us between chunks.)  The element-wise form, which
-// the compiler cannot keep free of spills in the loop, launches per chunk.
-template <typename T, bool DMA, int AK, int BKD>
-__global__ __launch_bounds__(256, 1) void lin_logits_ce_kernel(LogitsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  if constexpr (DMA) {
-    uint64_t* stats0 = a.stats;
-    for (int c = 0; c < a.nchunks; ++c) {
-      LogitsArgs ac = a;
-      ac.row0 = (int64_t)c * a.rt_chunk * 256;
-      ac.rtc = min(a.rt_chunk, a.rt_total - c * a.rt_chunk);
-      ac.stats = stats0 + (size_t)c * a.rt_chunk * 256 * a.nvt * 2;
-      // a thread index the compiler cannot see through, so nothing
-      // lane-dependent is hoisted out of this loop and held across a tile
-      int tid = (int)threadIdx.x;
-      asm volatile("" : "+v"(tid));
-      logits_ce_tile<T, DMA, AK, BKD>(ac, lds, tid, a.rt_chunk);
-      __syncthreads();  // the LDS is free for the next chunk's K loop
+  // e in the input format: each wave stages its 128 x 128 quarter in LDS
+  // (rows of 272 bytes), 32 rows at a time, and writes them out as 16-byte
+  // vectors, so the stores of one block overlap the conversions of the next.
+  constexpr int kGS = 136;  // staged row stride in elements
+  uint16_t* stg = (uint16_t*)(lds + 16384 + wave * (128 * kGS * 2));
+  uint16_t* stg_l = stg + 4 * (lane >> 5) * kGS + (lane & 31);  // + kRowOff(i, v) * kGS + 32 j
+  const int64_t cbase = (int64_t)n0 + wn * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x16 blk = t.acc[i][j];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(blk[v]);
     }
-  } else {
-    logits_ce_tile<T, DMA, AK, BKD>(a, lds, (int)threadIdx.x, a.rtc);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = i * 32 + q * 4 + (lane >> 4), cv = (lane & 15) * 8;
+      const int64_t R = mrow0 + wm * 128 + rr;
+      const int64_t c = cbase + cv;
+      if (R < a.N && c < a.ldg) *(lg::u32x4*)(a.g + R * a.ldg + c) = *(const lg::u32x4*)(stg + rr * kGS + cv);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3-4. dh = g W and dW = g^T h (16-bit): MFMA tiles, 2^-k on output.
+// 3. per row (a workgroup walks rows R = blockIdx.x, + gridDim.x, ...): the
+// row's log-sum-exp from its tiles' (c, sum) pairs, merged in a fixed order,
+// the row's loss (lse - x_y, or log1p(S / e^{x_y}) when p_y <= 1/2, S the
+// label-excluded sum), and g = s (softmax - onehot) written over the stored
+// e, rounded once more to the input format: e s 2^(c - lse log2 e) off the
+// label, -s (1 - p_y) on it; +0 on ignored rows, NaN on rows with a label
+// outside [0, V) (+0 past the vocabulary).
+// ---------------------------------------------------------------------------
+struct RescaleArgs {
+  const int64_t* labels;
+  int64_t ignore;
+  int64_t N, V;
+  int nvt;
+  uint16_t* g;
+  int64_t ldg;
+  const float2* tstats;
+  const float* xy;
+  const LinHeader* hdr;
+  float* loss_rows;
+};
+
+constexpr int kMaxRescaleTiles = 8192;  // dynamic LDS: two floats per tile
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+__device__ __forceinline__ float from_bits(uint32_t b);
+template <>
+__device__ __forceinline__ float from_bits<__bf16>(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+template <>
+__device__ __forceinline__ float from_bits<_Float16>(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void lin_rescale_kernel(RescaleArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  float* tc = (float*)lds;   // [nvt] the tiles' c, then their factors s 2^(c - L)
+  float* tsum = tc + a.nvt;  // [nvt] the tiles' sums
+  __shared__ float red[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nvec = (int)(a.ldg >> 3);
+  const float gs = a.hdr->gscale;
+  const uint32_t nanb = to_bits<T>(__builtin_nanf(""));
+  for (int64_t R = blockIdx.x; R < a.N; R += gridDim.x) {
+    const int64_t y = a.labels[R];
+    uint16_t* grow = a.g + R * a.ldg;
+    if (y == a.ignore || y < 0 || y >= a.V) {  // the same for the whole workgroup
+      const bool ign = (y == a.ignore);
+      for (int q = tid; q < nvec; q += 256) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t c = (int64_t)q * 8 + 2 * k;
+          const uint32_t lo = (!ign && c < a.V) ? nanb : 0u, hi = (!ign && c + 1 < a.V) ? nanb : 0u;
+          wv[k] = lo | (hi << 16);
+        }
+        __builtin_nontemporal_store(lg::u32x4{wv[0], wv[1], wv[2], wv[3]}, (lg::u32x4*)(grow + (int64_t)q * 8));
+      }
+      if (tid == 0) a.loss_rows[R] = ign ? 0.0f : __builtin_nanf("");
+      continue;
+    }
+    const float2* ts = a.tstats + R * a.nvt;
+    const float xyv = a.xy[R];
+    float mx = -INFINITY;
+    for (int v = tid; v < a.nvt; v += 256) {
+      const float2 p = ts[v];
+      tc[v] = p.x;
+      tsum[v] = p.y;
+      mx = fmaxf(mx, p.x);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    const float Mc = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float sl = 0.0f;
+    for (int v = tid; v < a.nvt; v += 256) {
+      const float c = tc[v];
+      if (c != -INFINITY) sl += tsum[v] * __builtin_amdgcn_exp2f(c - Mc);
+    }
+    sl = wave_sum(sl);
+    if (lane == 0) red[4 + wave] = sl;
+    __syncthreads();
+    // S: the label-excluded sum, ey the label's term, both relative to 2^Mc
+    const float S = (red[4] + red[5]) + (red[6] + red[7]);
+    const float ey = __builtin_amdgcn_exp2f(xyv * kLog2e - Mc);
+    const float St = S + ey;
+    const float L = Mc + log2f(St);  // lse log2 e
+    const float pcomp = S / St;      // 1 - p_y
+    if (tid == 0) a.loss_rows[R] = (pcomp >= 0.5f) ? (L * kLn2 - xyv) : log1pf(S / ey);
+    for (int v = tid; v < a.nvt; v += 256) {
+      const float c = tc[v];
+      tc[v] = (c == -INFINITY) ? 0.0f : gs * __builtin_amdgcn_exp2f(c - L);
+    }
+    __syncthreads();
+    const uint32_t gyb = to_bits<T>(-gs * pcomp);
+    const int yq = (int)(y >> 3), ys = (int)(y & 7) * 16;
+    // four 16-byte vectors per lane in flight, then their products
+    for (int q0 = tid; q0 < nvec; q0 += 1024) {
+      lg::u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 256 * u;
+        if (q < nvec) v[u] = *(const lg::u32x4*)(grow + (int64_t)q * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 256 * u;
+        if (q < nvec) {
+          const float f = tc[q >> 5];  // 32 vectors per 256-column tile
+          uint32_t o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t wd = v[u][k];
+            o[k] = to_bits<T>(from_bits<T>(wd & 0xFFFFu) * f) | ((uint32_t)to_bits<T>(from_bits<T>(wd >> 16) * f) << 16);
+          }
+          if (q == yq) {
+            const int k = ys >> 5, sh = ys & 16;
+            o[k] = (o[k] & ~(0xFFFFu << sh)) | (gyb << sh);
+          }
+          __builtin_nontemporal_store(lg::u32x4{o[0], o[1], o[2], o[3]}, (lg::u32x4*)(grow + (int64_t)q * 8));
+        }
+      }
+    }
+    __syncthreads();  // tc / red are rewritten for the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4-5. dh = g W and dW = g^T h (16-bit): MFMA tiles, 2^-k on output.
 // ---------------------------------------------------------------------------
 // LDS of the direct-to-LDS backward kernels: the K loop's stages, then the
 // epilogue's four 128 x 136 staged quarters
@@ -872,42 +767,34 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
   la.N = N;
   la.H = H;
   la.V = V;
+  la.mt = (int)((N + 255) / 256);
   la.nvt = L.nvt;
-  la.hdr = hdr;
+  la.eshift = fp16 ? 14.0f : 0.0f;
   la.g = g;
   la.ldg = L.ldg;
-  la.xy = (uint64_t*)(ws + L.xy);
-  la.lse = (uint64_t*)(ws + L.lse);
-  la.pc = (uint64_t*)(ws + L.pc);
-  la.loss_rows = loss_rows;
-  const int64_t rt_total = (N + 255) / 256;
-  auto kfn = fast ? lin_logits_ce_kernel<T, true, lg::kKC, lg::kKC> : lin_logits_ce_kernel<T, false, lg::kKCg, lg::kKCg>;
-  const int lds_bytes = kLogitsLds;
-  if (set_lds(kfn, lds_bytes) != CE_OK) return CE_ERR_HIP;
-  la.rt_chunk = L.rt_chunk;
-  la.nchunks = L.nchunks;
-  la.rt_total = (int)rt_total;
-  if (fast) {
-    la.row0 = 0;
-    la.rtc = L.rt_chunk;
-    la.stats = (uint64_t*)(ws + L.stats);
-    void* params[] = {&la};
-    if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(L.rt_chunk * L.nvt)), dim3(256), params, lds_bytes,
-                                   st) != hipSuccess)
-      return CE_ERR_HIP;
-  } else {
-    for (int c = 0; c < L.nchunks; ++c) {
-      const int64_t rt0 = (int64_t)c * L.rt_chunk;
-      const int rtc = (int)((rt_total - rt0 < L.rt_chunk) ? rt_total - rt0 : L.rt_chunk);
-      la.row0 = rt0 * 256;
-      la.rtc = rtc;
-      la.stats = (uint64_t*)(ws + L.stats) + (size_t)c * L.rt_chunk * 256 * L.nvt * 2;
-      void* params[] = {&la};
-      if (hipLaunchCooperativeKernel((const void*)kfn, dim3((unsigned)(rtc * L.nvt)), dim3(256), params, lds_bytes,
-                                     st) != hipSuccess)
-        return CE_ERR_HIP;
-    }
-  }
+  la.tstats = (float2*)(ws + L.tstats);
+  la.xy = (float*)(ws + L.xy);
+  auto kfn = fast ? lin_logits_kernel<T, true> : lin_logits_kernel<T, false>;
+  if (set_lds(kfn, kLogitsLds) != CE_OK) return CE_ERR_HIP;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)((int64_t)la.mt * L.nvt)), dim3(256), kLogitsLds, st, la);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  RescaleArgs ra;
+  ra.labels = labels;
+  ra.ignore = ignore;
+  ra.N = N;
+  ra.V = V;
+  ra.nvt = L.nvt;
+  ra.g = g;
+  ra.ldg = L.ldg;
+  ra.tstats = la.tstats;
+  ra.xy = la.xy;
+  ra.hdr = hdr;
+  ra.loss_rows = loss_rows;
+  const int rs_lds = 2 * L.nvt * 4;
+  if (set_lds(lin_rescale_kernel<T>, rs_lds) != CE_OK) return CE_ERR_HIP;
+  hipLaunchKernelGGL(lin_rescale_kernel<T>, dim3((unsigned)(N < (1 << 20) ? N : (1 << 20))), dim3(256), rs_lds, st,
+                     ra);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   if (gh) {  // dh [N, H] = g [N, V] W [V, H]
     BwdArgs b;
     b.A = (const char*)g;
@@ -1018,8 +905,8 @@ size_t workspace_for(int64_t N, int64_t H, int64_t V, int64_t chunk_rows, int dt
     const F32Layout L = f32_layout(N, V, chunk_rows);
     return L.ce_ws_bytes ? L.total : 0;
   }
-  const int64_t cus = device_cus();
-  return fast_layout(N, V, cus > 0 ? cus : 256).total;
+  if ((V + 255) / 256 > kMaxRescaleTiles) return 0;
+  return fast_layout(N, V).total;
 }
 
 }  // namespace
@@ -1077,9 +964,7 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
     return run_f32((const float*)hidden, ld_hidden, (const float*)weight, ld_weight, labels, N, H, V, ignore_index,
                    dloss, loss_mean, loss_rows, n_valid, status, (float*)grad_hidden, ld_grad_hidden,
                    (float*)grad_weight, ld_grad_weight, ws, f32_layout(N, V, chunk_rows), st);
-  const int64_t cus = device_cus();
-  const FastLayout L = fast_layout(N, V, cus > 0 ? cus : 256);
-  if (L.nvt > (cus > 0 ? cus : 256)) return CE_ERR_UNSUPPORTED;  // a row tile's vocabulary tiles must be co-resident
+  const FastLayout L = fast_layout(N, V);
   if (dtype == CE_DTYPE_BF16)
     return run_fast<__bf16>(hidden, ld_hidden, weight, ld_weight, labels, N, H, V, ignore_index, dloss, loss_mean,
                             loss_rows, n_valid, status, grad_hidden, ld_grad_hidden, grad_weight, ld_grad_weight, ws,

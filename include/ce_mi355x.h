@@ -223,13 +223,14 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  * kernels (16-bit inputs, fp32 accumulation, no other library).  The logits
  * are never stored: each 256 x 256 tile of them stays in the registers of
  * the workgroup that computed it, whose epilogue takes per row the tile's
- * max and label-excluded sum of exponentials (fp32), merges them with the
- * row's other vocabulary tiles through the workspace (a bounded wait; on
- * expiry CE_STATUS_SYNC_TIMEOUT and NaN results), writes loss_rows (fp32:
- * lse - x_y, or log1p(S / e^{x_y}) when p_y > 1/2) and turns the tile into
- * its part of g, rounded once to dtype.  All tiles of a chunk of rows are
- * resident at once (a cooperative launch): 256 floor(CUs / ceil(vocab / 256))
- * rows per chunk (512 with vocab 32000 on 256 CUs; chunk_rows is not used).
+ * max m and stores the tile's exponentials e = exp(x - m) (times 2^14 for
+ * fp16), rounded to dtype, with 0 at the label's column, where g goes, and
+ * per row the tile's shift and label-excluded sum of e -- the statistics of
+ * 256-column chunks.  A second kernel merges each row's pairs into its
+ * log-sum-exp (fixed order), writes loss_rows (fp32: lse - x_y, or
+ * log1p(S / e^{x_y}) when p_y > 1/2) and turns the row's e into
+ * g = dloss (softmax - onehot) / n_valid by its tiles' factors, rounded to
+ * dtype again (the label's element, -dloss (1 - p_y) / n_valid, once).
  * g is held scaled by 2^k (k = 0 for bf16; for fp16, k puts dloss / n_valid
  * near 2^14 so that g stays in range) and the two backward products remove
  * the scale before rounding grad_hidden and grad_weight once to dtype.
@@ -237,7 +238,8 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  * Fast operand loads (16-byte direct-to-LDS) need hidden and weight rows
  * 16-byte aligned (pointer and ld * element size) and hidden_size a multiple
  * of 8; other layouts load element by element (same results, slower).
- * vocab above 256 x CUs (65536 on MI355X) gives CE_ERR_UNSUPPORTED.
+ * chunk_rows is not used.  vocab above 2097152 (8192 tiles of 256) gives
+ * CE_ERR_UNSUPPORTED.
  * fp32: chunk_rows rows at a time (0 = 1024; rounded up to a multiple of 64,
  * and up so that there are at most 4096 chunks): the chunk's fp32 logits by
  * an fp32 tiled product, its loss and gradient by the kernels of
@@ -254,15 +256,14 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  *   grad_weight   out or NULL: vocab rows, stride ld_grad_weight (all zeros when
  *                 n_rows == 0).
  *   workspace     ce_linear_workspace_bytes(...) bytes, 256-byte aligned,
- *                 zeroed once with ce_workspace_init and then owned by this
- *                 function (calls on one workspace must not overlap, and it
- *                 is not shared with the cross-entropy entry points).
- *                 bf16 / fp16: a 256-byte header (the call's epoch, scale and
- *                 status), g (n_rows x vocab rounded up to 8, dtype), the
- *                 per-row tile statistics of the largest chunk and three
- *                 n_rows x 8-byte exchange arrays (label logit, lse,
- *                 1 - p_y).  fp32: a chunk's cross-entropy workspace, the
- *                 chunk's fp32 logits and per-chunk counts.
+ *                 owned by this function for the call (calls on one
+ *                 workspace must not overlap).  bf16 / fp16: a 256-byte
+ *                 header (the call's scale and status), g (n_rows x vocab
+ *                 rounded up to 8, dtype), two floats per row and 256-column
+ *                 tile, and the label logits (n_rows floats); nothing in it
+ *                 carries over between calls.  fp32: a chunk's cross-entropy
+ *                 workspace (zeroed at the start of every call), the chunk's
+ *                 fp32 logits and per-chunk counts.
  * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
  * dimension of 2^31 or more, or operands whose byte extent reaches 2^31
  * (the loads use 32-bit buffer offsets), give CE_ERR_UNSUPPORTED; a failed

@@ -165,9 +165,9 @@ def linear(lib, hidden=FAKE, ldh=64, weight=FAKE, ldw=64, labels=FAKE, N=8, H=64
 
 def test_linear_workspace_bytes(lib):
     b = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_BF16)
-    # 16-bit: the batch's gradient g in the input format and the small tagged
-    # exchange arrays -- no fp32 logits, no transposed copies
-    assert 4096 * 32000 * 2 <= b < 4096 * 32000 * 2 + (64 << 20)
+    # 16-bit: the batch's gradient g in the input format and two floats per row
+    # and 256-column tile -- no fp32 logits, no transposed copies
+    assert 4096 * 32000 * 2 + 4096 * 125 * 8 <= b < 4096 * 32000 * 2 + (8 << 20)
     assert lib.ce_linear_workspace_bytes(4096, 4096, 32000, 64, 1) == b  # chunk_rows does not enter
     f32 = lib.ce_linear_workspace_bytes(4096, 4096, 32000, 1024, _lib.CE_DTYPE_F32)
     assert 1024 * 32000 * 4 <= f32 < 1024 * 32000 * 4 + (64 << 20)  # one fp32 chunk of logits
@@ -177,6 +177,10 @@ def test_linear_workspace_bytes(lib):
     assert lib.ce_linear_workspace_bytes(4, 64, 10, -1, 1) == 0
     assert lib.ce_linear_workspace_bytes(4, 64, 10, 0, 5) == 0
     assert lib.ce_linear_workspace_bytes(4, 64, 1 << 31, 0, 1) == 0
+    # 16-bit: up to 8192 vocabulary tiles of 256 per row
+    assert lib.ce_linear_workspace_bytes(4, 64, 8192 * 256, 0, 1) > 0
+    assert lib.ce_linear_workspace_bytes(4, 64, 8192 * 256 + 1, 0, 1) == 0
+    assert lib.ce_linear_workspace_bytes(4, 64, 8192 * 256 + 1, 0, _lib.CE_DTYPE_F32) > 0
 
 
 @pytest.mark.parametrize("kw,code", [
