@@ -304,18 +304,35 @@ __global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
   // test.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // the block's row shifts and label columns for this lane's 16 rows
+    // (rows rb + 8 k + u, v = 4 k + u), as four 16-byte reads each
+    const int rb = wm * 128 + i * 32 + 4 * (lane >> 5);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    float mcv[16];
+    int ycv[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 qm = *(const f32x4*)(mrowc + rb + 8 * k);
+      const i32x4 qy = *(const i32x4*)(yrel + rb + 8 * k);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mcv[4 * k + u] = qm[u];
+        ycv[4 * k + u] = qy[u];
+      }
+    }
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = lg::acc_row(wm, i, v, lane);
-      const float mc = mrowc[r];
+      const float mc = mcv[v];
       float e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -mc));
         if (!full) e[j] = cvalid[j] ? e[j] : 0.0f;
       }
-      const int d = yrel[r] - lc;         // the label's column is this lane's in block d / 32
+      const int d = ycv[v] - lc;          // the label's column is this lane's in block d / 32
       const bool own = (d & ~0x60) == 0;  // d in {0, 32, 64, 96}
       if (__ballot(own) != 0) {
         float xv = 0.0f;
