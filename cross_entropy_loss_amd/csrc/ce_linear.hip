@@ -269,18 +269,17 @@ __global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float m[16];
-    if (full) {
+    if (__builtin_expect(full, 1)) {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         m[v] = fmaxf(fmaxf(t.acc[i][0][v], t.acc[i][1][v]), fmaxf(t.acc[i][2][v], t.acc[i][3][v]));
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) m[v] = -INFINITY;
+      for (int v = 0; v < 16; ++v) {
+        float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16 blk = t.acc[i][j];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) m[v] = fmaxf(m[v], cvalid[j] ? blk[v] : -INFINITY);
+        for (int j = 0; j < 4; ++j) x[j] = cvalid[j] ? t.acc[i][j][v] : -INFINITY;
+        m[v] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       }
     }
 #pragma unroll
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t.acc[i][j][v], kLog2e, -mc));
-        if (!full) e[j] = cvalid[j] ? e[j] : 0.0f;
+        e[j] = cvalid[j] ? e[j] : 0.0f;  // all true in every tile but the last
       }
       const int d = ycv[v] - lc;          // the label's column is this lane's in block d / 32
       const bool own = (d & ~0x60) == 0;  // d in {0, 32, 64, 96}
@@ -382,6 +381,7 @@ __global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
       for (int v = 0; v < 16; ++v) stg_l[kRowOff(i, v) * kGS + 32 * j] = to_bits<T>(blk[v]);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+    asm volatile("" ::: "memory");       // and the compiler keeps the 16-bit writes before the 16-byte reads
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = i * 32 + q * 4 + (lane >> 4), cv = (lane & 15) * 8;
@@ -574,6 +574,7 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
         for (int v = 0; v < 16; ++v)
           stg[lg::acc_row(0, i, v, lane) * kGS + lg::acc_col(0, j, lane)] = to_bits<T>(t.acc[i][j][v] * us);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (it reads only its own quarter)
+    asm volatile("" ::: "memory");       // and the compiler keeps the 16-bit writes before the 16-byte reads
     const int cb = n0 + wn * 128;
 #pragma unroll 4
     for (int q = 0; q < 32; ++q) {
