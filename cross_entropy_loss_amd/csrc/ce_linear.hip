@@ -961,10 +961,14 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
   if (!fits32(N) || !fits32(H) || !fits32(V) || !fits32(ld_hidden) || !fits32(ld_weight) ||
       !fits32(ld_grad_hidden) || !fits32(ld_grad_weight))
     return CE_ERR_UNSUPPORTED;
-  // buffer resources address each operand with 32-bit offsets below 2^31
+  // buffer resources address h and W with 32-bit offsets below 2^31; g too
+  // in the element-wise loads (one resource over all of g's rows) and the fp32
+  // path, not in the direct-to-LDS ones (resources per tile or per K step)
   const int64_t lim = (int64_t)1 << 31;
+  const bool fast16 = dtype != CE_DTYPE_F32 && aligned16(hidden, ld_hidden, 2) && aligned16(weight, ld_weight, 2) &&
+                      H % 8 == 0;
   if ((N + 256) * ld_hidden * es >= lim || (V + 256) * ld_weight * es >= lim ||
-      (N + 256) * ((V + 7) / 8 * 8) * es >= lim)
+      (!fast16 && (N + 256) * ((V + 7) / 8 * 8) * es >= lim))
     return CE_ERR_UNSUPPORTED;
   const size_t need = workspace_for(N, H, V, chunk_rows, dtype);
   if (need == 0) return CE_ERR_UNSUPPORTED;

@@ -265,9 +265,10 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  *                 workspace (zeroed at the start of every call), the chunk's
  *                 fp32 logits and per-chunk counts.
  * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
- * dimension of 2^31 or more, or operands whose byte extent reaches 2^31
- * (the loads use 32-bit buffer offsets), give CE_ERR_UNSUPPORTED; a failed
- * launch gives CE_ERR_HIP.
+ * dimension of 2^31 or more, hidden or weight of 2^31 bytes or more (the
+ * loads use 32-bit buffer offsets), and for fp32 or the element-wise loads
+ * also (n_rows + 256) x vocab elements of 2^31 bytes or more, give
+ * CE_ERR_UNSUPPORTED; a failed launch gives CE_ERR_HIP.
  */
 size_t ce_linear_workspace_bytes(int64_t n_rows, int64_t hidden_size, int64_t vocab, int64_t chunk_rows,
                                  int dtype);

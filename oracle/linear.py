@@ -92,3 +92,47 @@ def linear_cross_entropy(hidden: np.ndarray, weight: np.ndarray, labels: np.ndar
     return {"loss_mean": L, "loss_rows": loss, "n_valid": n, "bad": int(bad.sum()), "scale": scale,
             "grad_logits64": g, "grad_hidden64": gh, "grad_weight64": gw,
             "grad_hidden": round_to(gh, dtype), "grad_weight": round_to(gw, dtype)}
+
+
+def linear_sampled(hidden: np.ndarray, weight: np.ndarray, labels: np.ndarray, dtype: str, rows, cols,
+                   ignore_index: int = -100, dloss: float = 1.0, row_block: int = 512) -> dict:
+    """The same definition as ``linear_cross_entropy`` for shapes whose full
+    [N, V] float64 arrays do not fit: the rows are taken ``row_block`` at a
+    time (each row's softmax depends on its own logits only), and only the
+    requested outputs are kept -- every row's loss, dL/dh for the rows in
+    ``rows`` and dL/dW for the vocabulary rows in ``cols``, whose sums over the
+    tokens are accumulated block by block (float64; only the order of that sum
+    differs from ``linear_cross_entropy``), and the softmax's columns ``cols``
+    for every row.
+    """
+    h = widen(hidden, dtype)
+    w = widen(weight, dtype)
+    y = np.asarray(labels, np.int64).reshape(-1)
+    N, V = h.shape[0], w.shape[0]
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    valid = y != ignore_index
+    n = int(valid.sum())
+    scale = dloss / n if n else float("nan")
+    loss = np.zeros(N, np.float64)
+    gh = np.zeros((len(rows), h.shape[1]), np.float64)
+    gw = np.zeros((len(cols), h.shape[1]), np.float64)
+    pc = np.zeros((N, len(cols)), np.float64)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        lb, p, _, vb, bad = forward64(h[r0:r1], w, y[r0:r1], ignore_index)
+        loss[r0:r1] = lb
+        pc[r0:r1] = p[:, cols]
+        g = np.zeros_like(p)
+        good = vb & ~bad
+        rr = np.nonzero(good)[0]
+        g[rr] = scale * p[rr]
+        g[rr, y[r0:r1][rr]] -= scale
+        g[bad] = np.nan
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        if len(sel):
+            gh[sel] = g[rows[sel] - r0] @ w
+        gw += g[:, cols].T @ h[r0:r1]
+    L = float(np.sum(loss[valid]) / n) if n else float("nan")
+    return {"loss_mean": L, "loss_rows": loss, "n_valid": n, "scale": scale, "grad_hidden64": gh,
+            "grad_weight64": gw, "softmax_cols": pc}

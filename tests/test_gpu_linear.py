@@ -230,3 +230,58 @@ def test_linear_many_row_tiles():
     # 17 row tiles: two full groups of 8 in the tile order and a group of one, ragged
     h, w, y = make(28, 4100, 64, 1000, "bf16")
     check(run(h, w, y, "bf16"), h, w, y, "bf16")
+
+
+def test_linear_llama3_vocab_full_size():
+    # the 128k-vocabulary head at the benchmark's full size (8192 x 4096 x 128256 bf16; g alone is 2.1 GB):
+    # every row's loss, 24 rows of dL/dh and 24 vocabulary rows of dL/dW against the row-blocked oracle,
+    # with the bounds of check() (the logits' error E_i bounded through Cauchy-Schwarz,
+    # gamma_H |h_i|_2 max_v |W_v|_2, which needs no [N, V] product)
+    import workloads as wl
+    lw = wl.LINEAR_WORKLOADS[2]
+    h, w, y = wl.linear_inputs(lw)
+    out = run(h, w, y, lw.dtype, dloss=lw.dloss)
+    assert int(out["status"].item()) == 0
+    rng = np.random.default_rng(29)
+    N, V = len(y), w.shape[0]
+    rows = np.sort(rng.choice(N, 24, replace=False))
+    cols = np.unique(np.concatenate([y[rows[:12]][y[rows[:12]] >= 0], rng.choice(V, 12, replace=False)]))
+    _say(f"  oracle over {N} rows in blocks (rows {rows[:4]}..., {len(cols)} vocabulary rows)")
+    ref = lin.linear_sampled(h, w, y, lw.dtype, rows, cols, dloss=lw.dloss)
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    hx, wx = oracle.widen(h, lw.dtype), oracle.widen(w, lw.dtype)
+    g16, u = 2.0 ** -24, U[lw.dtype]
+    E = lw.H * g16 * np.linalg.norm(hx, axis=1) * np.linalg.norm(wx, axis=1).max()
+    valid = y != -100
+    lr = out["loss_rows"].cpu().numpy().astype(np.float64)
+    tol = 2 * E + 2.0 ** -23 * np.abs(ref["loss_rows"]) + 1e-30
+    err = np.abs(lr - ref["loss_rows"])
+    assert (err[valid] <= tol[valid]).all(), f"loss rows: max err/tol {np.max(err[valid] / tol[valid])}"
+    assert (lr[~valid] == 0).all()
+    L = float(out["loss_mean"].item())
+    assert abs(L - ref["loss_mean"]) <= np.sum(2 * E[valid]) / ref["n_valid"] + 2.0 ** -22 * abs(ref["loss_mean"])
+    s, rg = ref["scale"], 2 * u + u * u
+    # |g| <= s (p + onehot) on valid rows
+    _, p_rows, _, _, _ = lin.forward64(hx[rows], wx, y[rows])
+    aw = np.abs(wx)
+    onehot_w = np.where((valid[rows] & (y[rows] >= 0))[:, None], aw[np.clip(y[rows], 0, V - 1)], 0.0)
+    sp_rows = np.where(valid[rows][:, None], s * p_rows, 0.0)
+    A = sp_rows @ aw + s * onehot_w
+    B = (2.1 * E[rows][:, None] * sp_rows) @ aw
+    got = oracle.widen(host_bits(out["grad_hidden"][torch.from_numpy(rows).cuda()], lw.dtype), lw.dtype)
+    want = ref["grad_hidden64"]
+    bound = (rg + V * g16) * A + B + u * np.abs(want) + TINY[lw.dtype]
+    d = np.abs(got - want)
+    assert (d <= bound).all(), f"grad_hidden rows: worst err/bound {(d / bound).max():.3f}"
+    _say(f"  grad_hidden rows: worst err/bound {(d / bound).max():.3f}")
+    pc = np.where(valid[:, None], ref["softmax_cols"], 0.0)
+    hit = (y[:, None] == cols[None, :]) & valid[:, None]
+    ah = np.abs(hx)
+    A = s * (pc + hit).T @ ah
+    B = (2.1 * s * E[:, None] * pc).T @ ah
+    got = oracle.widen(host_bits(out["grad_weight"][torch.from_numpy(cols).cuda()], lw.dtype), lw.dtype)
+    want = ref["grad_weight64"]
+    bound = (rg + N * g16) * A + B + u * np.abs(want) + TINY[lw.dtype]
+    d = np.abs(got - want)
+    assert (d <= bound).all(), f"grad_weight rows: worst err/bound {(d / bound).max():.3f}"
+    _say(f"  grad_weight rows: worst err/bound {(d / bound).max():.3f}")

@@ -123,6 +123,28 @@ def test_gradient_sums_and_scale():
     assert np.all(r1["grad_hidden64"][ign] == 0)
 
 
+@pytest.mark.parametrize("dtype,block", [("bf16", 7), ("f16", 64), ("f32", 1)])
+def test_row_blocked_form_matches_the_whole(dtype, block):
+    # linear_sampled takes the rows a block at a time and keeps some outputs; it must give the whole
+    # computation's loss rows and the selected rows of dL/dh and dL/dW (which it sums block by block)
+    h, w, y = _case(11, 40, 12, 50, dtype)
+    y[3] = 50  # a bad label: NaN row, NaN in every dL/dW row
+    whole = lin.linear_cross_entropy(h, w, y, dtype, dloss=0.7)
+    rows, cols = [0, 3, 17, 39], [0, 5, 49]
+    part = lin.linear_sampled(h, w, y, dtype, rows, cols, dloss=0.7, row_block=block)
+    assert part["n_valid"] == whole["n_valid"]
+    np.testing.assert_array_equal(np.isnan(part["loss_rows"]), np.isnan(whole["loss_rows"]))
+    # numpy's product may sum a one-row block in another order: float64 rounding apart, the same
+    np.testing.assert_allclose(part["loss_rows"], whole["loss_rows"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(part["grad_hidden64"], whole["grad_hidden64"][rows], rtol=1e-12, atol=1e-18)
+    assert np.isnan(part["grad_weight64"]).all() and np.isnan(whole["grad_weight64"][cols]).all()
+    y[3] = 1
+    whole = lin.linear_cross_entropy(h, w, y, dtype, dloss=0.7)
+    part = lin.linear_sampled(h, w, y, dtype, rows, cols, dloss=0.7, row_block=block)
+    np.testing.assert_allclose(part["grad_weight64"], whole["grad_weight64"][cols], rtol=1e-12, atol=1e-18)
+    assert part["loss_mean"] == pytest.approx(whole["loss_mean"], rel=1e-15)
+
+
 def test_no_valid_rows_and_bad_label():
     h, w, y = _case(10, 5, 4, 6, "bf16")
     r = lin.linear_cross_entropy(h, w, np.full(5, -100), "bf16")
