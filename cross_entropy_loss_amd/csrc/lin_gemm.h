@@ -640,19 +640,9 @@ __device__ __forceinline__ int xcd_order(int bid, int total) {
   return x * per + (x < extra ? x : extra) + q;
 }
 
-// Tile order for a grid of mt x nt tiles: each XCD walks whole columns of row
-// tiles, so the mt row tiles that share one B tile (a slab of the weight) run
-// on one XCD, close in time, and the B tile is fetched into that XCD's L2
-// once.
-__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& m_tile, int& n_tile) {
-  const int lin = xcd_order(bid, mt * nt);
-  n_tile = lin / mt;
-  m_tile = lin % mt;
-}
-
-// The same with each XCD walking whole rows of column tiles: the nt column
-// tiles that share one A tile run on one XCD (for products whose A operand
-// is the larger one).
+// Tile order for a grid of mt x nt tiles: each XCD walks whole rows of column
+// tiles, so the nt column tiles that share one A tile run on one XCD (for
+// products whose A operand is the larger one).
 __device__ __forceinline__ void tile_of_rows(int bid, int mt, int nt, int& m_tile, int& n_tile) {
   const int lin = xcd_order(bid, mt * nt);
   m_tile = lin / nt;
