@@ -195,9 +195,9 @@ struct LogitsArgs {
 };
 
 // LDS: the K loop's stages (128 KB, or 64 KB for the element-wise loop),
-// then the epilogue's row data (4 KB), its statistics transpose (65 KB at
-// offset 16 KB) and, after it, four staged 128 x 136 quarters of e (136 KB
-// at offset 16 KB).
+// then over them the epilogue's row data (4 KB) and its statistics transpose
+// (65 KB at offset 16 KB), and once the statistics are out, four staged
+// 128 x 136 quarters of e (136 KB, also at offset 16 KB).
 constexpr int kLogitsLds = 160 * 1024;
 static_assert(16384 + 4 * 128 * 136 * 2 <= kLogitsLds, "staged quarters");
 static_assert(16384 + 256 * 65 * 4 <= kLogitsLds, "statistics transpose");
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void lin_logits_kernel(LogitsArgs a) {
 // ---------------------------------------------------------------------------
 // 3. per row (a workgroup walks rows R = blockIdx.x, + gridDim.x, ...): the
 // row's log-sum-exp from its tiles' (c, sum) pairs, merged in a fixed order,
-// the row's loss (lse - x_y, or log1p(S / e^{x_y}) when p_y <= 1/2, S the
+// the row's loss (lse - x_y, or log1p(S / e^{x_y}) when p_y > 1/2, S the
 // label-excluded sum), and g = s (softmax - onehot) written over the stored
 // e, rounded once more to the input format: e s 2^(c - lse log2 e) off the
 // label, -s (1 - p_y) on it; +0 on ignored rows, NaN on rows with a label
