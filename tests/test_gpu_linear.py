@@ -285,3 +285,11 @@ def test_linear_llama3_vocab_full_size():
     d = np.abs(got - want)
     assert (d <= bound).all(), f"grad_weight rows: worst err/bound {(d / bound).max():.3f}"
     _say(f"  grad_weight rows: worst err/bound {(d / bound).max():.3f}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_linear_wide_logit_range(dtype):
+    # logits spread ~25 (weights 12x the default): within a tile the exponentials relative to its max span
+    # fp16's subnormals (e is stored times 2^14) and far below, and the tiles' shifts differ widely
+    h, w, y = make(31, 300, 64, 5000, dtype, sigma_w=25.0 / math.sqrt(64))
+    check(run(h, w, y, dtype, dloss=2.0), h, w, y, dtype, dloss=2.0)
