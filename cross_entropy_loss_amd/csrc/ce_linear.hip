@@ -69,16 +69,32 @@ struct LinHeader {
 static_assert(sizeof(LinHeader) == 256, "header size");
 
 struct FastLayout {
-  size_t g, tstats, xy, total;
+  size_t g, tstats, xy, part, total;
   int64_t ldg;  // g's row stride: vocab rounded up to 8 elements
   int nvt;      // vocabulary tiles of 256
+  int dh_split; // K ranges of dh = g W (1: no split)
+  int dh_kc;    // vocabulary columns per range (a multiple of 32)
 };
 
-FastLayout fast_layout(int64_t N, int64_t V) {
+// dh has ceil(N / 256) x ceil(H / 256) tiles, each over all V columns of g:
+// with few rows that leaves most of the chip idle, so the vocabulary is cut
+// into ranges (each at least 1024 columns) until the tiles times the ranges
+// fill 256 workgroups; every range writes an fp32 partial tile, summed in
+// range order by a small kernel.
+void dh_split_of(int64_t N, int64_t H, int64_t V, int& split, int& kc) {
+  const int64_t tiles = ((N + 255) / 256) * ((H + 255) / 256);
+  int s = 1;
+  while (s < 16 && tiles * s < 256 && V / (2 * s) >= 1024) s *= 2;
+  kc = (int)((V + 32 * s - 1) / (32 * s) * 32);
+  split = (int)((V + kc - 1) / kc);
+}
+
+FastLayout fast_layout(int64_t N, int64_t H, int64_t V) {
   FastLayout L;
   memset(&L, 0, sizeof(L));
   L.ldg = (V + 7) / 8 * 8;
   L.nvt = (int)((V + 255) / 256);
+  dh_split_of(N, H, V, L.dh_split, L.dh_kc);
   size_t off = sizeof(LinHeader);
   L.g = align256(off);
   off = L.g + align256((size_t)N * L.ldg * 2);
@@ -86,6 +102,8 @@ FastLayout fast_layout(int64_t N, int64_t V) {
   off += align256((size_t)N * L.nvt * 8);
   L.xy = off;  // [row] the label's logit
   off += align256((size_t)N * 4);
+  L.part = off;  // dh's fp32 partial tiles, [range][N][H], when split
+  if (L.dh_split > 1) off += align256((size_t)L.dh_split * N * H * 4);
   L.total = off;
   return L;
 }
@@ -540,6 +558,8 @@ struct BwdArgs {
   int64_t ldc;
   int vec_out;  // C 16-byte aligned, ldc and N multiples of 8
   const LinHeader* hdr;
+  int ksplit, kc;  // K ranges of kc columns (ksplit 1: the whole K, C written directly)
+  float* part;     // ksplit > 1: fp32 partial tiles [range][M][N] instead of C
 };
 
 // DMA: both operands through direct-to-LDS loads (16-byte aligned rows;
@@ -548,17 +568,37 @@ struct BwdArgs {
 template <typename T, int AK, int BKD, bool DMA>
 __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int mt = (a.M + 255) / 256, nt = (a.N + 255) / 256;
-  int mti, nti;
-  // g (the A operand of both products) is the larger operand: its tiles are
-  // shared within an XCD
-  lg::tile_of_rows(blockIdx.x, mt, nt, mti, nti);
+  const int mt = (a.M + 255) / 256, nt = (a.N + 255) / 256, tiles = mt * nt;
+  // g (the A operand of both products) is the larger operand: the tiles of
+  // a K range that share its rows are neighbours in the XCD order
+  int lin = lg::xcd_order((int)blockIdx.x, tiles * a.ksplit);
+  const int ks = lin / tiles;
+  lin -= ks * tiles;
+  const int mti = lin / nt, nti = lin % nt;
   const int m0 = mti * 256, n0 = nti * 256;
+  // this workgroup's K range: columns k0 .. k0 + kr of A and B
+  const int64_t k0 = (int64_t)ks * a.kc;
+  const int kr = (int)(a.K - k0 < a.kc ? a.K - k0 : a.kc);
+  const char* A = a.A + (AK == lg::kKC ? k0 * 2 : k0 * a.lda * 2);
+  const char* B = a.B + (BKD == lg::kKC ? k0 * 2 : k0 * a.ldb * 2);
   Tile t;
-  if constexpr (DMA) lg::tile_dma<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.Mx, a.Nx, a.K, m0, n0);
-  else lg::tile_rs<T, AK, BKD>(t, lds, a.A, a.lda, a.B, a.ldb, a.M, a.N, a.K, m0, n0);
+  if constexpr (DMA) lg::tile_dma<T, AK, BKD>(t, lds, A, a.lda, B, a.ldb, a.Mx, a.Nx, kr, m0, n0);
+  else lg::tile_rs<T, AK, BKD>(t, lds, A, a.lda, B, a.ldb, a.M, a.N, kr, m0, n0);
   const float us = a.hdr->unscale;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  if (a.ksplit > 1) {  // the range's fp32 partial tile; the sum, the scale and the rounding come later
+    float* P = a.part + (size_t)ks * a.M * a.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int R = m0 + lg::acc_row(wm, i, v, lane), c = n0 + lg::acc_col(wn, j, lane);
+          if (R < a.M && c < a.N) P[(int64_t)R * a.N + c] = t.acc[i][j][v];
+        }
+    return;
+  }
   if constexpr (DMA) {
     // Each wave stages its 128 x 128 quarter in LDS (rows of 272 bytes) and
     // writes it out as 16-byte vectors (8 elements; a.vec_out: C 16-byte
@@ -604,6 +644,35 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_kernel(BwdArgs a) {
         if (c < a.N) crow[c] = to_bits<T>(t.acc[i][j][v] * us);
       }
     }
+}
+
+// The split dh: C = us (sum over the K ranges of the partial tiles, in range
+// order), rounded once; four columns per thread (N a multiple of 4).
+template <typename T>
+__global__ __launch_bounds__(256) void lin_split_sum_kernel(const float* part, int ksplit, int M, int N,
+                                                            const LinHeader* hdr, uint16_t* C, int64_t ldc,
+                                                            int vec_out) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const float us = hdr->unscale;
+  const int64_t n4 = N / 4, total = (int64_t)M * n4, plane = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / n4, c = (i - r * n4) * 4;
+    const float* p = part + r * N + c;
+    f32x4 acc = *(const f32x4*)p;
+    for (int k = 1; k < ksplit; ++k) acc += *(const f32x4*)(p + k * plane);
+    uint16_t* d = C + r * ldc + c;
+    const uint32_t w0 = (uint32_t)to_bits<T>(acc[0] * us) | ((uint32_t)to_bits<T>(acc[1] * us) << 16);
+    const uint32_t w1 = (uint32_t)to_bits<T>(acc[2] * us) | ((uint32_t)to_bits<T>(acc[3] * us) << 16);
+    if (vec_out) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *(u32x2*)d = u32x2{w0, w1};
+    } else {
+      d[0] = (uint16_t)w0;
+      d[1] = (uint16_t)(w0 >> 16);
+      d[2] = (uint16_t)w1;
+      d[3] = (uint16_t)(w1 >> 16);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -828,12 +897,23 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.ldc = ldgh;
     b.vec_out = aligned16(gh, ldgh, 2) && H % 8 == 0;
     b.hdr = hdr;
+    const int split = fast ? L.dh_split : 1;  // K ranges (direct-to-LDS path only)
+    b.ksplit = split;
+    b.kc = split > 1 ? L.dh_kc : (int)V;
+    b.part = split > 1 ? (float*)(ws + L.part) : nullptr;
     auto fn = fast ? lin_bwd_kernel<T, lg::kKC, lg::kKO, true> : lin_bwd_kernel<T, lg::kKC, lg::kKOg, false>;
     const int lb = fast ? kBwdLds : 2 * lg::kStageBytes;
     if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
-    const int64_t grid = ((N + 255) / 256) * ((H + 255) / 256);
+    const int64_t grid = ((N + 255) / 256) * ((H + 255) / 256) * split;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lb, st, b);
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+    if (split > 1) {
+      const int64_t quads = N * H / 4, blocks = (quads + 255) / 256;
+      hipLaunchKernelGGL(lin_split_sum_kernel<T>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
+                         (const float*)b.part, split, (int)N, (int)H, (const LinHeader*)hdr, (uint16_t*)gh, ldgh,
+                         b.vec_out);
+      if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+    }
   }
   if (gw) {  // dW [V, H] = g^T h: A(v, tok) = g[tok][v], B(h, tok) = h[tok][h]
     BwdArgs b;
@@ -850,6 +930,9 @@ int run_fast(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, c
     b.ldc = ldgw;
     b.vec_out = aligned16(gw, ldgw, 2) && H % 8 == 0;
     b.hdr = hdr;
+    b.ksplit = 1;  // ceil(V / 256) x ceil(H / 256) tiles fill the chip
+    b.kc = (int)N;
+    b.part = nullptr;
     auto fn = fast ? lin_bwd_kernel<T, lg::kKO, lg::kKO, true> : lin_bwd_kernel<T, lg::kKO, lg::kKOg, false>;
     const int lb = fast ? kBwdLds : 2 * lg::kStageBytes;
     if (set_lds(fn, lb) != CE_OK) return CE_ERR_HIP;
@@ -924,7 +1007,7 @@ size_t workspace_for(int64_t N, int64_t H, int64_t V, int64_t chunk_rows, int dt
     return L.ce_ws_bytes ? L.total : 0;
   }
   if ((V + 255) / 256 > kMaxRescaleTiles) return 0;
-  return fast_layout(N, V).total;
+  return fast_layout(N, H, V).total;
 }
 
 }  // namespace
@@ -986,7 +1069,7 @@ int ce_linear_fwd_bwd(const void* hidden, int64_t ld_hidden, const void* weight,
     return run_f32((const float*)hidden, ld_hidden, (const float*)weight, ld_weight, labels, N, H, V, ignore_index,
                    dloss, loss_mean, loss_rows, n_valid, status, (float*)grad_hidden, ld_grad_hidden,
                    (float*)grad_weight, ld_grad_weight, ws, f32_layout(N, V, chunk_rows), st);
-  const FastLayout L = fast_layout(N, V);
+  const FastLayout L = fast_layout(N, H, V);
   if (dtype == CE_DTYPE_BF16)
     return run_fast<__bf16>(hidden, ld_hidden, weight, ld_weight, labels, N, H, V, ignore_index, dloss, loss_mean,
                             loss_rows, n_valid, status, grad_hidden, ld_grad_hidden, grad_weight, ld_grad_weight, ws,

@@ -260,8 +260,10 @@ int ce_fwd_bwd_inplace_noalloc(void* logits, int64_t ld, const int64_t* labels, 
  *                 workspace must not overlap).  bf16 / fp16: a 256-byte
  *                 header (the call's scale and status), g (n_rows x vocab
  *                 rounded up to 8, dtype), two floats per row and 256-column
- *                 tile, and the label logits (n_rows floats); nothing in it
- *                 carries over between calls.  fp32: a chunk's cross-entropy
+ *                 tile, the label logits (n_rows floats) and, when the rows
+ *                 are too few to fill the chip with dL/dh's tiles, fp32
+ *                 partial sums of dL/dh over up to 16 vocabulary ranges;
+ *                 nothing in it carries over between calls.  fp32: a chunk's cross-entropy
  *                 workspace (zeroed at the start of every call), the chunk's
  *                 fp32 logits and per-chunk counts.
  * Errors: as ce_fwd_bwd_inplace; n_rows, hidden_size, vocab or a leading
