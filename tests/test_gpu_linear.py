@@ -238,7 +238,7 @@ def test_linear_llama3_vocab_full_size():
     # with the bounds of check() (the logits' error E_i bounded through Cauchy-Schwarz,
     # gamma_H |h_i|_2 max_v |W_v|_2, which needs no [N, V] product)
     import workloads as wl
-    lw = wl.LINEAR_WORKLOADS[2]
+    lw = wl.LINEAR_WORKLOADS[4]
     h, w, y = wl.linear_inputs(lw)
     out = run(h, w, y, lw.dtype, dloss=lw.dloss)
     assert int(out["status"].item()) == 0

@@ -239,8 +239,8 @@ class LinearWorkload:
 LINEAR_WORKLOADS = {
     1: LinearWorkload("mistral7b-lmhead-b4s1024-bf16", 6, 4096, 4096, 32000, "bf16"),
     # a Llama-3-8B head (hidden 4096, vocabulary 128256) over the large-vocabulary cross-entropy
-    # shape's 8192 rows: g alone is 2.1 GB, the logits the fused path never stores
-    2: LinearWorkload("llama3-lmhead-b8s1024-bf16", 7, 8192, 4096, 128256, "bf16"),
+    # shape's 8192 rows (numbered as that shape, 4): g alone is 2.1 GB, the logits the fused path never stores
+    4: LinearWorkload("llama3-lmhead-b8s1024-bf16", 7, 8192, 4096, 128256, "bf16"),
 }
 
 
