@@ -830,7 +830,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="ce / split: 1-5 (default 2, 4096 x 32000 bf16); linear: 1 (4096 x 4096 x 32000, the "
+                         "default) or 4 (8192 x 4096 x 128256); rmsnorm / rope: 1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR")
