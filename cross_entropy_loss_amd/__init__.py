@@ -222,9 +222,10 @@ def _matrix(t: torch.Tensor, name: str):
 def ce_linear_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
                       chunk_rows: int = 0, dloss: torch.Tensor | None = None, workspace: Workspace | None = None,
                       want_grad_hidden: bool = True, want_grad_weight: bool = True) -> dict:
-    """LM-head projection + cross-entropy, forward and backward, token-chunked:
-    loss_mean, loss_rows, n_valid, status and (when asked for) grad_hidden,
-    grad_weight of dloss * L."""
+    """LM-head projection + cross-entropy, forward and backward (logits =
+    hidden weight^T, never stored for bf16 / fp16; fp32 goes chunk_rows rows
+    at a time): loss_mean, loss_rows, n_valid, status and (when asked for)
+    grad_hidden, grad_weight of dloss * L."""
     N, H, ldh = _matrix(hidden, "hidden")
     V, H2, ldw = _matrix(weight, "weight")
     if H2 != H or weight.dtype != hidden.dtype or weight.device != hidden.device:
