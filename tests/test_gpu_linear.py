@@ -24,6 +24,7 @@ far below them.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import numpy as np
@@ -293,3 +294,36 @@ def test_linear_wide_logit_range(dtype):
     # fp16's subnormals (e is stored times 2^14) and far below, and the tiles' shifts differ widely
     h, w, y = make(31, 300, 64, 5000, dtype, sigma_w=25.0 / math.sqrt(64))
     check(run(h, w, y, dtype, dloss=2.0), h, w, y, dtype, dloss=2.0)
+
+
+@pytest.mark.parametrize("N,V", [(256, 3000), (4096, 1500)])
+def test_linear_unaligned_grad_outputs(N, V):
+    # through the C ABI: grad_hidden and grad_weight one element past a 16-byte boundary with an odd row
+    # stride, so the products (and, with vocabulary 3000, dL/dh's sum over its two ranges) store element by
+    # element; the values must be those of the aligned call, bit for bit
+    H = 128
+    h, w, y = make(33 + N, N, H, V, "bf16")
+    ref = run(h, w, y, "bf16")
+    hd, wd = to_dev(h, "bf16"), to_dev(w, "bf16")
+    yd = torch.from_numpy(np.ascontiguousarray(y)).cuda()
+    ld = H + 3
+    gh_buf = torch.zeros(N * ld + 16, dtype=torch.bfloat16, device="cuda")
+    gw_buf = torch.zeros(V * ld + 16, dtype=torch.bfloat16, device="cuda")
+    lib = ce._lib.load()
+    nbytes = lib.ce_linear_workspace_bytes(N, H, V, 0, ce._lib.CE_DTYPE_BF16)
+    ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    outs = [torch.empty(1, dtype=torch.float32, device="cuda"), torch.empty(N, dtype=torch.float32, device="cuda"),
+            torch.empty(1, dtype=torch.int32, device="cuda"), torch.empty(1, dtype=torch.int32, device="cuda")]
+    P = lambda t, k=0: ctypes.c_void_p(t.data_ptr() + k)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = lib.ce_linear_fwd_bwd(P(hd), H, P(wd), H, P(yd), N, H, V, ce._lib.CE_DTYPE_BF16, -100, 0, None,
+                               P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), P(gh_buf, 2), ld, P(gw_buf, 2), ld,
+                               P(ws, off), nbytes, st)
+    assert rc == 0
+    torch.cuda.synchronize()
+    gh = gh_buf[1:1 + N * ld].view(N, ld)[:, :H]
+    gw = gw_buf[1:1 + V * ld].view(V, ld)[:, :H]
+    assert torch.equal(gh.view(torch.int16), ref["grad_hidden"].view(torch.int16))
+    assert torch.equal(gw.view(torch.int16), ref["grad_weight"].view(torch.int16))
+    assert torch.equal(outs[1], ref["loss_rows"])
