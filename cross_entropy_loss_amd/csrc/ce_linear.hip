@@ -78,13 +78,14 @@ struct FastLayout {
 
 // dh has ceil(N / 256) x ceil(H / 256) tiles, each over all V columns of g:
 // with few rows that leaves most of the chip idle, so the vocabulary is cut
-// into ranges (each at least 1024 columns) until the tiles times the ranges
-// fill 256 workgroups; every range writes an fp32 partial tile, summed in
-// range order by a small kernel.
+// into ranges (each at least 1024 columns), doubling their number while the
+// tiles times the ranges still fit in one round of 256 workgroups (a second
+// round would take as long as the ranges saved); every range writes an fp32
+// partial tile, summed in range order by a small kernel.
 void dh_split_of(int64_t N, int64_t H, int64_t V, int& split, int& kc) {
   const int64_t tiles = ((N + 255) / 256) * ((H + 255) / 256);
   int s = 1;
-  while (s < 16 && tiles * s < 256 && V / (2 * s) >= 1024) s *= 2;
+  while (s < 16 && tiles * 2 * s <= 256 && V / (2 * s) >= 1024) s *= 2;
   kc = (int)((V + 32 * s - 1) / (32 * s) * 32);
   split = (int)((V + kc - 1) / kc);
 }
